@@ -1,0 +1,168 @@
+"""Throughput of the fused linear cross-entropy forward + backward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload huge_vocab]
+
+One step = flce_forward + flce_backward (the whole hot path) over one batch of
+seeded synthetic inputs already resident in HBM.  The default workload is the
+262144-vocabulary / hidden-640 / 2048-token batch with softcap 30 (the
+configuration the metric is quoted on).  Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fused linear-CE fwd+bwd tokens/s on 1 MI355X; % of bf16 MFMA peak"
+PEAK_BF16_TFLOPS = 2500.0          # MI355X dense bf16 MFMA (published)
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="huge_vocab")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    return ap.parse_args()
+
+
+def cpu_baseline(w, inp, budget_s: float) -> dict:
+    """The CPU oracle (float64 numpy, as written) on a bounded sample of the
+    workload: consecutive 128-token blocks, each run as a batch of its own
+    (forward + backward incl. grad_weight), until the time budget is spent."""
+    import numpy as np
+    from oracle import Problem, backward, forward
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([d.get("num_threads", 1) for d in threadpool_info()
+                     if d.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    wt = inp.weight.float().numpy().astype(np.float64)
+    bias = None if inp.bias is None else inp.bias.numpy().astype(np.float64)
+    prob = Problem(logit_scale=w.logit_scale, softcap=w.softcap)
+    rows, blk = 0, 128
+    t0 = time.perf_counter()
+    while rows < w.n_tokens and time.perf_counter() - t0 < budget_s:
+        sl = slice(rows, min(w.n_tokens, rows + blk))
+        h = inp.hidden[sl].float().numpy().astype(np.float64)
+        t = inp.targets[sl].numpy()
+        go = inp.grad_out[sl].numpy() if w.reduction == "none" else inp.grad_out.numpy()
+        forward(h, wt, bias, t, prob)
+        backward(h, wt, bias, t, prob, w.reduction, go)
+        rows = sl.stop
+    dt = time.perf_counter() - t0
+    return {"value": rows / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"first {rows} of {w.n_tokens} tokens in 128-token batches, fwd+bwd "
+                      f"(float64 numpy), {dt:.1f} s"}
+
+
+def main() -> int:
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (got --gpus {args.gpus}); "
+              "the path's sharding is described in DESIGN.md", file=sys.stderr)
+        return 2
+    import torch
+
+    import linear_cross_entropy_fp32_amd as flce
+    from linear_cross_entropy_fp32_amd import _binding, synth
+
+    w = synth.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    inp = synth.make_inputs(w)
+    h = inp.hidden.to(dev)
+    wt = inp.weight.to(dev)
+    b = None if inp.bias is None else inp.bias.to(dev)
+    t = inp.targets.to(dev)
+    go = inp.grad_out.to(dev).reshape(-1)
+    n, hd, v = w.n_tokens, w.hidden, w.vocab
+    prob = _binding.problem_for(h, wt, w.logit_scale, w.softcap)
+    ws_bytes = flce.flce_workspace_bytes(prob)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    loss, lse, ent = (torch.empty(n, **f32) for _ in range(3))
+    hit = torch.empty(n, dtype=torch.uint8, device=dev)
+    red_f = torch.empty(3, **f32)
+    red_i = torch.empty(3, dtype=torch.int64, device=dev)
+    gh = torch.empty(n, hd, **f32)
+    gw = torch.empty(v, hd, **f32)
+    gb = torch.empty(v, **f32) if b is not None else None
+    mode = {"mean": 0, "sum": 1, "none": 2}[w.reduction]
+    L = flce.lib()
+    P = _binding._ptr
+    stream = torch.cuda.current_stream(dev)
+    sp = ctypes.c_void_p(stream.cuda_stream)
+
+    def fwd():
+        rc = L.flce_forward(ctypes.byref(prob), P(h), P(wt), P(b), P(t), P(loss), P(lse), P(ent),
+                            P(hit), None, P(red_f), P(red_i), P(ws), ws_bytes, sp)
+        if rc:
+            raise flce.FlceError(rc, flce.flce_last_error())
+
+    def bwd():
+        rc = L.flce_backward(ctypes.byref(prob), P(h), P(wt), P(b), P(t), P(lse), P(red_i), mode,
+                             P(go), P(gh), P(gw), P(gb), P(ws), ws_bytes, sp)
+        if rc:
+            raise flce.FlceError(rc, flce.flce_last_error())
+
+    for _ in range(args.warmup):
+        fwd()
+        bwd()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    start.record(stream)
+    for e0, e1, e2 in ev:
+        e0.record(stream)
+        fwd()
+        e1.record(stream)
+        bwd()
+        e2.record(stream)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    total_ms = start.elapsed_time(stop)
+    fwd_ms = sum(e0.elapsed_time(e1) for e0, e1, _ in ev) / args.steps
+    bwd_ms = sum(e1.elapsed_time(e2) for _, e1, e2 in ev) / args.steps
+    ms = total_ms / args.steps
+    flops = 8.0 * n * hd * v
+    tflops = flops / (ms * 1e-3) / 1e12
+    # dominant kernel: the forward call is one logit-tile kernel plus a merge
+    # of a few microseconds; its algorithmic work is 2*N*H*V flops per launch.
+    fwd_tflops = 2.0 * n * hd * v / (fwd_ms * 1e-3) / 1e12
+    out = {
+        "metric": METRIC, "value": n / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "n_tokens": n, "hidden": hd, "vocab": v,
+                   "hidden_dtype": w.hidden_dtype, "bias": w.bias, "logit_scale": w.logit_scale,
+                   "softcap": w.softcap, "reduction": w.reduction},
+        "tflops": tflops, "pct_bf16_peak": 100.0 * tflops / PEAK_BF16_TFLOPS,
+        "fwd_ms": fwd_ms, "bwd_ms": bwd_ms, "wall_s": wall,
+        "roofline": {"bound": "mfma", "kernel": "fwd_stats_kernel", "achieved": fwd_tflops,
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": fwd_tflops / PEAK_BF16_TFLOPS, "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,121 @@
+/*
+ * flce.h -- C ABI of the MI355X fused linear cross-entropy library (libflce.so).
+ *
+ * What is computed (TRL pull request "Add loss_type="cce", a fused linear
+ * cross-entropy loaded from the Hub": the description, "What it supports" and
+ * the review's "Correctness" facts):
+ *
+ *   z_raw[n, v] = sum_k hidden[n, k] * weight[v, k]   (fp32 accumulation)
+ *   z[n, v]     = softcap(logit_scale * (z_raw[n, v] + bias[v]))
+ *   softcap(x)  = c * tanh(x / c) when c = softcap > 0, else x
+ *   lse[n]      = log sum_v exp z[n, v]
+ *   loss[n]     = lse[n] - z[n, t_n]
+ *   entropy[n]  = lse[n] - sum_v p[n, v] z[n, v],  p = exp(z - lse)
+ *   argmax[n]   = lowest v with z[n, v] = max_v z[n, v];  hit[n] = (argmax == t_n)
+ *
+ * without ever storing the (tokens x vocab) logits, plus the backward
+ * grad_hidden / grad_weight / grad_bias.  Rows whose target equals
+ * ignore_index are still projected (the review's "Correctness" item 2) but
+ * carry no loss and no gradient.
+ *
+ * Conventions for every entry point:
+ *   - all tensor pointers are DEVICE pointers, row-major and contiguous;
+ *   - `stream` is a hipStream_t (passed as void*); all work is enqueued on it,
+ *     nothing is synchronised and no host<->device copy is made;
+ *   - the caller owns every buffer, including the workspace; the library
+ *     allocates nothing and keeps no state between calls, so calls are
+ *     re-entrant and the backward may be called any number of times;
+ *   - outputs are overwritten, never accumulated into;
+ *   - on error nothing is launched, a negative FLCE_ERR_* code is returned and
+ *     flce_last_error() (thread-local) describes it.
+ */
+#ifndef FLCE_H_
+#define FLCE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FLCE_OK 0
+#define FLCE_ERR_NULL (-1)      /* a required pointer is null */
+#define FLCE_ERR_SHAPE (-2)     /* N < 0, H < 8, H % 8 != 0, V < 1, or a size too large */
+#define FLCE_ERR_DTYPE (-3)     /* unsupported dtype combination (weight must be bf16) */
+#define FLCE_ERR_ALIGN (-4)     /* a pointer is not aligned as documented */
+#define FLCE_ERR_WORKSPACE (-5) /* workspace smaller than flce_workspace_bytes() */
+#define FLCE_ERR_HIP (-6)       /* a kernel launch failed */
+#define FLCE_ERR_ARG (-7)       /* a scalar argument is invalid (NaN scale, bad mode, ...) */
+
+#define FLCE_BF16 0
+#define FLCE_F32 1
+
+#define FLCE_GRAD_MEAN 0       /* grad_out[0] / divisor for every valid row */
+#define FLCE_GRAD_SUM 1        /* grad_out[0] for every valid row */
+#define FLCE_GRAD_PER_TOKEN 2  /* grad_out[n] for row n (reduction "none") */
+
+typedef struct flce_problem {
+  int64_t n_tokens;      /* N >= 0 rows of hidden / targets                      */
+  int64_t hidden;        /* H >= 8, H % 8 == 0                                    */
+  int64_t vocab;         /* V >= 1 rows of weight                                 */
+  int32_t hidden_dtype;  /* FLCE_BF16 or FLCE_F32 (fp32 hidden states)            */
+  int32_t weight_dtype;  /* FLCE_BF16 (the lm_head is cast to bf16 by the caller) */
+  float logit_scale;     /* s, finite; 1 = off                                    */
+  float softcap;         /* c, final_logit_softcapping; <= 0 = off                */
+  int64_t ignore_index;  /* usually -100                                          */
+  float mean_divisor;    /* > 0: the mean divides by it (num_items_in_batch);
+                            otherwise by n_valid.  0 valid rows -> mean 0.        */
+  int32_t reserved;      /* must be 0                                             */
+} flce_problem;
+
+/* Check the problem description only (no HIP call).  0 or FLCE_ERR_*. */
+int flce_validate(const flce_problem* p);
+
+/* Bytes of device workspace one forward or backward call needs (the same
+ * buffer serves both).  Returns 0 and sets *bytes on success. */
+int flce_workspace_bytes(const flce_problem* p, size_t* bytes);
+
+/* Forward.
+ *   hidden   [N, H]  bf16 or fp32 (per p->hidden_dtype), 16-byte aligned
+ *   weight   [V, H]  bf16, 16-byte aligned
+ *   bias     [V]     fp32, or NULL for no bias
+ *   targets  [N]     int64; ignore_index marks ignored rows; a value outside
+ *                    [0, V) that is not ignore_index is treated as ignored and
+ *                    counted in reduced_i64[2]
+ * Outputs (all required except argmax):
+ *   loss, lse, entropy [N] fp32 (loss and entropy are 0 on ignored rows; lse
+ *                    is always written), hit [N] uint8, argmax [N] int32 or NULL,
+ *   reduced_f32 [3]: loss_sum, loss_mean, entropy_sum (over valid rows)
+ *   reduced_i64 [3]: n_valid, n_correct, n_bad_target
+ * workspace: >= flce_workspace_bytes(), 256-byte aligned. */
+int flce_forward(const flce_problem* p, const void* hidden, const void* weight,
+                 const float* bias, const int64_t* targets, float* loss, float* lse,
+                 float* entropy, uint8_t* hit, int32_t* argmax, float* reduced_f32,
+                 int64_t* reduced_i64, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Backward of the reduced loss.
+ *   lse [N] and reduced_i64 [3] are the forward's outputs for the same inputs
+ *   (n_valid is read on the device for FLCE_GRAD_MEAN; no host sync).
+ *   grad_mode: FLCE_GRAD_MEAN / FLCE_GRAD_SUM read grad_out[0];
+ *              FLCE_GRAD_PER_TOKEN reads grad_out[0..N) (reduction "none").
+ * Outputs (fp32, overwritten): grad_hidden [N, H], grad_weight [V, H],
+ *   grad_bias [V] (may be NULL; must be NULL when bias is NULL).
+ * Entropy and accuracy are logged metrics and carry no gradient. */
+int flce_backward(const flce_problem* p, const void* hidden, const void* weight,
+                  const float* bias, const int64_t* targets, const float* lse,
+                  const int64_t* reduced_i64, int grad_mode, const float* grad_out,
+                  float* grad_hidden, float* grad_weight, float* grad_bias, void* workspace,
+                  size_t workspace_bytes, void* stream);
+
+/* Description of the last error on this thread ("" if none). */
+const char* flce_last_error(void);
+
+/* Library ABI version (bumped when a signature or struct changes). */
+int flce_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FLCE_H_ */

@@ -1,0 +1,11 @@
+"""MI355X fused linear cross-entropy: hidden @ lm_head.T (+ bias) * scale ->
+softcap -> loss / entropy / argmax accuracy and the backward, computed by HIP
+kernels in libflce.so without storing the (tokens x vocab) logits.
+
+The library is loaded on first use; if it has not been built, the first call
+raises (there is no fallback path).
+"""
+from ._binding import (FLCE_BF16, FLCE_F32, FLCE_GRAD_MEAN, FLCE_GRAD_PER_TOKEN,  # noqa: F401
+                       FLCE_GRAD_SUM, FlceError, FlceProblem, flce_backward, flce_forward,
+                       flce_last_error, flce_validate, flce_workspace_bytes, lib,
+                       linear_cross_entropy, make_problem)

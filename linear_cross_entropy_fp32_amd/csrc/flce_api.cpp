@@ -1,0 +1,373 @@
+// C-ABI host layer: argument validation, workspace planning and kernel
+// dispatch.  No allocation, no synchronisation, no state between calls.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "flce.h"
+#include "flce_internal.h"
+
+namespace flce {
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+constexpr int64_t kMaxRows = int64_t(1) << 30;
+constexpr int64_t kMaxHidden = int64_t(1) << 20;
+constexpr int64_t kMaxElems = int64_t(1) << 31;      // N*H and V*H stay int32-indexable per row
+constexpr size_t kAlign = 256;
+constexpr int64_t kTargetWgs = 2048;                 // ~8 workgroups per CU
+constexpr int64_t kDzChunkBytes = int64_t(1) << 28;  // vocab chunk of the staged backward
+
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline int64_t rup(int64_t a, int64_t b) { return cdiv(a, b) * b; }
+inline size_t aup(size_t a) { return (a + kAlign - 1) / kAlign * kAlign; }
+
+struct Plan {
+  int n_tok_tiles, n_voc_tiles, n_splits, tiles_per_split, fin_blocks;
+  int64_t vc;            // vocab chunk width of the backward (multiple of the tile)
+  int n_chunks;
+  int gh_splits;         // split-K of the grad_hidden contraction
+  int64_t gh_kps;
+  size_t off_hsplit, off_part, off_bsums, off_dz, off_ghpart;
+  size_t fwd_bytes, bwd_bytes, bytes;
+};
+
+int validate(const flce_problem* p) {
+  if (!p) return fail(FLCE_ERR_NULL, "problem is NULL");
+  if (p->reserved != 0) return fail(FLCE_ERR_ARG, "problem.reserved must be 0");
+  if (p->n_tokens < 0 || p->n_tokens > kMaxRows)
+    return fail(FLCE_ERR_SHAPE, "n_tokens=%lld out of range [0, 2^30]", (long long)p->n_tokens);
+  if (p->vocab < 1 || p->vocab > kMaxRows)
+    return fail(FLCE_ERR_SHAPE, "vocab=%lld out of range [1, 2^30]", (long long)p->vocab);
+  if (p->hidden < 8 || p->hidden > kMaxHidden || p->hidden % 8 != 0)
+    return fail(FLCE_ERR_SHAPE, "hidden=%lld must be a multiple of 8 in [8, 2^20]",
+                (long long)p->hidden);
+  if (p->n_tokens * p->hidden >= kMaxElems || p->vocab * p->hidden >= kMaxElems)
+    return fail(FLCE_ERR_SHAPE, "N*H or V*H exceeds 2^31 elements");
+  if (p->hidden_dtype != FLCE_BF16 && p->hidden_dtype != FLCE_F32)
+    return fail(FLCE_ERR_DTYPE, "hidden_dtype=%d unsupported (bf16 or fp32)", p->hidden_dtype);
+  if (p->weight_dtype != FLCE_BF16)
+    return fail(FLCE_ERR_DTYPE, "weight_dtype=%d unsupported: the lm_head must be bf16",
+                p->weight_dtype);
+  if (!std::isfinite(p->logit_scale))
+    return fail(FLCE_ERR_ARG, "logit_scale must be finite");
+  if (std::isnan(p->softcap) || std::isinf(p->softcap))
+    return fail(FLCE_ERR_ARG, "softcap must be finite (<= 0 disables it)");
+  if (std::isnan(p->mean_divisor) || std::isinf(p->mean_divisor))
+    return fail(FLCE_ERR_ARG, "mean_divisor must be finite");
+  return FLCE_OK;
+}
+
+Plan make_plan(const flce_problem* p) {
+  Plan pl{};
+  const int64_t n = p->n_tokens, h = p->hidden, v = p->vocab;
+  pl.n_tok_tiles = (int)cdiv(n, kLogitTileN);
+  pl.n_voc_tiles = (int)cdiv(v, kLogitTileV);
+  int64_t splits = n > 0 ? cdiv(kTargetWgs, pl.n_tok_tiles) : 1;
+  splits = std::max<int64_t>(1, std::min<int64_t>(splits, pl.n_voc_tiles));
+  pl.tiles_per_split = (int)cdiv(pl.n_voc_tiles, splits);
+  pl.n_splits = (int)cdiv(pl.n_voc_tiles, pl.tiles_per_split);
+  pl.fin_blocks = (int)cdiv(n, 256);
+
+  // backward: vocab chunks of about kDzChunkBytes of bf16 dz
+  int64_t vc = n > 0 ? (kDzChunkBytes / (2 * n)) / kLogitTileV * kLogitTileV : rup(v, kLogitTileV);
+  vc = std::max<int64_t>(vc, kLogitTileV);
+  vc = std::min<int64_t>(vc, rup(v, kLogitTileV));
+  pl.vc = vc;
+  pl.n_chunks = (int)cdiv(v, vc);
+  const int64_t gh_tiles = cdiv(n, kGemmTileM) * cdiv(h, kGemmTileN);
+  const int64_t kloop = std::min<int64_t>(vc, v);
+  int64_t ghs = gh_tiles > 0 ? cdiv(1024, gh_tiles) : 1;
+  ghs = std::max<int64_t>(1, std::min<int64_t>(ghs, cdiv(kloop, 256)));
+  pl.gh_kps = rup(cdiv(kloop, ghs), 64);
+  pl.gh_splits = (int)cdiv(kloop, pl.gh_kps);
+
+  size_t off = 0;
+  pl.off_hsplit = off;
+  if (p->hidden_dtype == FLCE_F32) off += aup(size_t(2) * n * h * 2);
+  const size_t shared_end = off;
+  pl.off_part = off;
+  off += aup(size_t(pl.n_splits) * n * sizeof(PartState));
+  pl.off_bsums = off;
+  off += aup(size_t(std::max(pl.fin_blocks, 1)) * sizeof(BlockSums));
+  pl.fwd_bytes = off;
+  off = shared_end;
+  pl.off_dz = off;
+  off += aup(size_t(n) * vc * 2);
+  pl.off_ghpart = off;
+  if (pl.gh_splits > 1) off += aup(size_t(pl.gh_splits) * n * h * 4);
+  pl.bwd_bytes = off;
+  pl.bytes = std::max(pl.fwd_bytes, pl.bwd_bytes);
+  return pl;
+}
+
+bool aligned(const void* ptr, size_t a) { return (reinterpret_cast<uintptr_t>(ptr) % a) == 0; }
+
+// final-logit constants (see final_u() in the kernels)
+void logit_consts(const flce_problem* p, float& kx, float& c1, float& c2) {
+  const double log2e = 1.4426950408889634;
+  if (p->softcap > 0) {
+    kx = (float)(2.0 * p->logit_scale * log2e / p->softcap);
+    c1 = (float)(p->softcap * log2e);
+    c2 = (float)(2.0 * p->softcap * log2e);
+  } else {
+    kx = (float)(p->logit_scale * log2e);
+    c1 = c2 = 0.f;
+  }
+}
+
+int hip_check(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(FLCE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return FLCE_OK;
+}
+
+}  // namespace
+}  // namespace flce
+
+using namespace flce;
+
+extern "C" {
+
+int flce_abi_version(void) { return 1; }
+
+const char* flce_last_error(void) { return g_err; }
+
+int flce_validate(const flce_problem* p) {
+  g_err[0] = 0;
+  return validate(p);
+}
+
+int flce_workspace_bytes(const flce_problem* p, size_t* bytes) {
+  g_err[0] = 0;
+  if (!bytes) return fail(FLCE_ERR_NULL, "bytes is NULL");
+  const int rc = validate(p);
+  if (rc) return rc;
+  *bytes = make_plan(p).bytes;
+  return FLCE_OK;
+}
+
+int flce_forward(const flce_problem* p, const void* hidden, const void* weight,
+                 const float* bias, const int64_t* targets, float* loss, float* lse,
+                 float* entropy, uint8_t* hit, int32_t* argmax, float* reduced_f32,
+                 int64_t* reduced_i64, void* workspace, size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  int rc = validate(p);
+  if (rc) return rc;
+  const int64_t n = p->n_tokens;
+  if (!weight || !reduced_f32 || !reduced_i64 || !workspace)
+    return fail(FLCE_ERR_NULL, "weight, reduced outputs and workspace are required");
+  if (n > 0 && (!hidden || !targets || !loss || !lse || !entropy || !hit))
+    return fail(FLCE_ERR_NULL, "hidden, targets and per-token outputs are required");
+  if ((hidden && !aligned(hidden, 16)) || !aligned(weight, 16))
+    return fail(FLCE_ERR_ALIGN, "hidden and weight must be 16-byte aligned");
+  if ((bias && !aligned(bias, 4)) || (targets && !aligned(targets, 8)) ||
+      (loss && !aligned(loss, 4)) || (lse && !aligned(lse, 4)) ||
+      (entropy && !aligned(entropy, 4)) || (argmax && !aligned(argmax, 4)) ||
+      !aligned(reduced_f32, 4) || !aligned(reduced_i64, 8))
+    return fail(FLCE_ERR_ALIGN, "bias/targets/outputs misaligned for their dtype");
+  if (!aligned(workspace, kAlign)) return fail(FLCE_ERR_ALIGN, "workspace must be 256-byte aligned");
+  const Plan pl = make_plan(p);
+  if (workspace_bytes < pl.bytes)
+    return fail(FLCE_ERR_WORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes,
+                pl.bytes);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+
+  const uint16_t* h0 = static_cast<const uint16_t*>(hidden);
+  const uint16_t* h1 = nullptr;
+  if (p->hidden_dtype == FLCE_F32 && n > 0) {
+    uint16_t* hi = reinterpret_cast<uint16_t*>(ws + pl.off_hsplit);
+    uint16_t* lo = hi + n * p->hidden;
+    if ((rc = hip_check(launch_split_hidden(static_cast<const float*>(hidden), hi, lo,
+                                            n * p->hidden, s), "split_hidden")))
+      return rc;
+    h0 = hi;
+    h1 = lo;
+  }
+  PartState* part = reinterpret_cast<PartState*>(ws + pl.off_part);
+  if (n > 0) {
+    FwdArgs a{};
+    a.w = static_cast<const uint16_t*>(weight);
+    a.h0 = h0;
+    a.h1 = h1;
+    a.bias = bias;
+    a.tgt = targets;
+    a.n = (int)n;
+    a.hdim = (int)p->hidden;
+    a.v = (int)p->vocab;
+    logit_consts(p, a.kx, a.c1, a.c2);
+    a.n_tok_tiles = pl.n_tok_tiles;
+    a.n_splits = pl.n_splits;
+    a.tiles_per_split = pl.tiles_per_split;
+    a.n_voc_tiles = pl.n_voc_tiles;
+    a.part = part;
+    if ((rc = hip_check(launch_fwd_stats(a, p->softcap > 0, s), "fwd_stats"))) return rc;
+  }
+  FinalArgs f{};
+  f.part = part;
+  f.n_splits = pl.n_splits;
+  f.n = (int)n;
+  f.v = (int)p->vocab;
+  f.tgt = targets;
+  f.ignore_index = p->ignore_index;
+  f.loss = loss;
+  f.lse = lse;
+  f.entropy = entropy;
+  f.hit = hit;
+  f.argmax = argmax;
+  f.block_sums = reinterpret_cast<BlockSums*>(ws + pl.off_bsums);
+  return hip_check(launch_fwd_finalize(f, pl.fin_blocks, p->mean_divisor > 0 ? p->mean_divisor : 0.f,
+                                       reduced_f32, reduced_i64, s),
+                   "fwd_finalize");
+}
+
+int flce_backward(const flce_problem* p, const void* hidden, const void* weight,
+                  const float* bias, const int64_t* targets, const float* lse,
+                  const int64_t* reduced_i64, int grad_mode, const float* grad_out,
+                  float* grad_hidden, float* grad_weight, float* grad_bias, void* workspace,
+                  size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  int rc = validate(p);
+  if (rc) return rc;
+  const int64_t n = p->n_tokens, h = p->hidden, v = p->vocab;
+  if (grad_mode < FLCE_GRAD_MEAN || grad_mode > FLCE_GRAD_PER_TOKEN)
+    return fail(FLCE_ERR_ARG, "grad_mode=%d invalid", grad_mode);
+  if (!weight || !grad_weight || !workspace || !reduced_i64 || !grad_out)
+    return fail(FLCE_ERR_NULL, "weight, grad_weight, reduced_i64, grad_out and workspace are required");
+  if (n > 0 && (!hidden || !targets || !lse || !grad_hidden))
+    return fail(FLCE_ERR_NULL, "hidden, targets, lse and grad_hidden are required");
+  if (grad_bias && !bias) return fail(FLCE_ERR_ARG, "grad_bias given without bias");
+  if ((hidden && !aligned(hidden, 16)) || !aligned(weight, 16))
+    return fail(FLCE_ERR_ALIGN, "hidden and weight must be 16-byte aligned");
+  if ((bias && !aligned(bias, 4)) || (targets && !aligned(targets, 8)) ||
+      (lse && !aligned(lse, 4)) || !aligned(reduced_i64, 8) || !aligned(grad_out, 4) ||
+      (grad_hidden && !aligned(grad_hidden, 4)) || !aligned(grad_weight, 4) ||
+      (grad_bias && !aligned(grad_bias, 4)))
+    return fail(FLCE_ERR_ALIGN, "inputs/outputs misaligned for their dtype");
+  if (!aligned(workspace, kAlign)) return fail(FLCE_ERR_ALIGN, "workspace must be 256-byte aligned");
+  const Plan pl = make_plan(p);
+  if (workspace_bytes < pl.bytes)
+    return fail(FLCE_ERR_WORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes,
+                pl.bytes);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+
+  if (n == 0) {
+    if ((rc = hip_check(launch_fill_zero(grad_weight, v * h, s), "fill_zero"))) return rc;
+    if (grad_bias && (rc = hip_check(launch_fill_zero(grad_bias, v, s), "fill_zero"))) return rc;
+    return FLCE_OK;
+  }
+
+  const uint16_t* h0 = static_cast<const uint16_t*>(hidden);
+  const uint16_t* h1 = nullptr;
+  if (p->hidden_dtype == FLCE_F32) {
+    uint16_t* hi = reinterpret_cast<uint16_t*>(ws + pl.off_hsplit);
+    uint16_t* lo = hi + n * h;
+    if ((rc = hip_check(launch_split_hidden(static_cast<const float*>(hidden), hi, lo, n * h, s),
+                        "split_hidden")))
+      return rc;
+    h0 = hi;
+    h1 = lo;
+  }
+  uint16_t* dz = reinterpret_cast<uint16_t*>(ws + pl.off_dz);
+  float* ghpart = reinterpret_cast<float*>(ws + pl.off_ghpart);
+
+  DzArgs d{};
+  d.w = static_cast<const uint16_t*>(weight);
+  d.h0 = h0;
+  d.h1 = h1;
+  d.bias = bias;
+  d.tgt = targets;
+  d.lse = lse;
+  d.red_i64 = reduced_i64;
+  d.grad_out = grad_out;
+  d.mode = grad_mode;
+  d.mean_divisor = p->mean_divisor > 0 ? p->mean_divisor : 0.f;
+  d.scale = p->logit_scale;
+  d.n = (int)n;
+  d.hdim = (int)h;
+  d.v = (int)v;
+  d.ignore_index = p->ignore_index;
+  logit_consts(p, d.kx, d.c1, d.c2);
+  d.n_tok_tiles = pl.n_tok_tiles;
+  d.dz = dz;
+  d.ldz = pl.vc;
+
+  for (int c = 0; c < pl.n_chunks; ++c) {
+    const int64_t c0 = int64_t(c) * pl.vc;
+    const int64_t width = std::min<int64_t>(pl.vc, v - c0);
+    d.c0 = (int)c0;
+    const int tiles = (int)cdiv(width, kLogitTileV);
+    if ((rc = hip_check(launch_bwd_dz(d, tiles, p->softcap > 0, s), "bwd_dz"))) return rc;
+
+    // grad_hidden[n, :] (+)= sum_v dz[n, v] W[c0 + v, :]
+    GemmArgs g{};
+    g.a_ptr = dz;
+    g.lda = pl.vc;
+    g.a_row_bound = (int)n;
+    g.a_k_bound = (int)pl.vc;
+    g.b_ptr = static_cast<const uint16_t*>(weight) + c0 * h;
+    g.ldb = h;
+    g.b_row_bound = (int)h;
+    g.b_k_bound = (int)width;
+    g.n_tiles = (int)cdiv(h, kGemmTileN);
+    g.k_len = (int)width;
+    g.k_per_split = (int)pl.gh_kps;
+    g.c = pl.gh_splits > 1 ? ghpart : grad_hidden;
+    g.ldc = h;
+    g.c_split_stride = n * h;
+    g.m_store = (int)n;
+    g.n_store = (int)h;
+    g.accumulate = c > 0;
+    if ((rc = hip_check(launch_gemm_store(g, (int)cdiv(n, kGemmTileM), pl.gh_splits, true, s),
+                        "gemm_grad_hidden")))
+      return rc;
+
+    // grad_weight[c0 + v, :] = sum_n dz[n, v] h[n, :]
+    GemmArgs gw{};
+    gw.a_ptr = dz;
+    gw.lda = pl.vc;
+    gw.a_row_bound = (int)pl.vc;
+    gw.a_k_bound = (int)n;
+    gw.b_ptr = h0;
+    gw.ldb = h;
+    gw.b_row_bound = (int)h;
+    gw.b_k_bound = (int)n;
+    gw.n_tiles = (int)cdiv(h, kGemmTileN);
+    gw.k_len = (int)n;
+    gw.k_per_split = (int)rup(n, 64);
+    gw.c = grad_weight + c0 * h;
+    gw.ldc = h;
+    gw.c_split_stride = 0;
+    gw.m_store = (int)width;
+    gw.n_store = (int)h;
+    gw.accumulate = 0;
+    if ((rc = hip_check(launch_gemm_store(gw, (int)cdiv(width, kGemmTileM), 1, false, s),
+                        "gemm_grad_weight")))
+      return rc;
+
+    if (grad_bias &&
+        (rc = hip_check(launch_colsum(dz, pl.vc, (int)n, (int)width, grad_bias + c0, s), "colsum")))
+      return rc;
+  }
+  if (pl.gh_splits > 1 &&
+      (rc = hip_check(launch_sum_partials(ghpart, pl.gh_splits, n * h, grad_hidden, n * h, s),
+                      "sum_partials")))
+    return rc;
+  return FLCE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,105 @@
+"""Shared helpers of the GPU parity tests: run the library through the C ABI
+on seeded inputs and compare with the CPU oracle at the stated tolerances.
+
+Tolerances (fixed for this method, not tuned): per-token loss, entropy and
+lse within 2e-3 absolute; reduced loss and entropy sum within 1e-4 relative;
+grad_hidden / grad_weight / grad_bias within 1e-2 relative Frobenius error and
+exactly zero where the oracle's gradient is exactly zero; argmax and hit exact
+on every row whose oracle top-2 margin is at least 1e-2.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import linear_cross_entropy_fp32_amd as flce
+from linear_cross_entropy_fp32_amd import synth
+from oracle import Problem
+
+TOL_TOKEN = 2e-3
+TOL_REDUCED = 1e-4
+TOL_GRAD = 1e-2
+MARGIN = 1e-2
+MODES = {"mean": flce.FLCE_GRAD_MEAN, "sum": flce.FLCE_GRAD_SUM,
+         "none": flce.FLCE_GRAD_PER_TOKEN}
+
+
+def say(msg: str) -> None:
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def to_f64(t):
+    return None if t is None else t.detach().float().cpu().numpy().astype(np.float64) \
+        if t.dtype != torch.float64 else t.detach().cpu().numpy()
+
+
+def prob_of(w: synth.Workload, mean_divisor: float = 0.0) -> Problem:
+    return Problem(logit_scale=w.logit_scale, softcap=w.softcap, mean_divisor=mean_divisor)
+
+
+def run_gpu(w: synth.Workload, inp: synth.Inputs, mean_divisor: float = 0.0,
+            backward: bool = True, dev: str = "cuda:0") -> dict:
+    """Forward (+ backward) through the C ABI; returns CPU tensors."""
+    h = inp.hidden.to(dev)
+    wt = inp.weight.to(dev)
+    b = None if inp.bias is None else inp.bias.to(dev)
+    t = inp.targets.to(dev)
+    f = flce.flce_forward(h, wt, t, b, w.logit_scale, w.softcap, -100, mean_divisor)
+    out = {k: (v.cpu() if v is not None else None) for k, v in f.items()}
+    if backward:
+        go = inp.grad_out.to(dev).reshape(-1)
+        gh, gw, gb = flce.flce_backward(h, wt, t, f["lse"], f["reduced_i64"], MODES[w.reduction],
+                                        go, b, w.logit_scale, w.softcap, -100, mean_divisor)
+        out["grad_hidden"] = gh.cpu()
+        out["grad_weight"] = gw.cpu()
+        out["grad_bias"] = None if gb is None else gb.cpu()
+    torch.cuda.synchronize()
+    return out
+
+
+def rel_fro(a: np.ndarray, b: np.ndarray) -> float:
+    nb = float(np.linalg.norm(b))
+    if nb == 0.0:
+        return 0.0 if float(np.abs(a).max(initial=0.0)) == 0.0 else float("inf")
+    return float(np.linalg.norm(a - b)) / nb
+
+
+def check_tokens(g: dict, o: dict, rows=None, label: str = "") -> None:
+    sel = slice(None) if rows is None else rows
+    for k in ("loss", "entropy", "lse"):
+        d = np.abs(g[k].numpy().astype(np.float64)[sel] - o[k])
+        assert d.max(initial=0.0) <= TOL_TOKEN, f"{label} {k}: max |diff| {d.max()}"
+    sure = o["margin"] >= MARGIN
+    gam = g["argmax"].numpy()[sel]
+    assert np.array_equal(gam[sure], o["argmax"][sure]), f"{label} argmax differs on sure rows"
+    ghit = g["hit"].numpy()[sel]
+    valid = o["valid"] if "valid" in o else None
+    if valid is not None:
+        assert np.all(ghit[~valid] == 0), f"{label} hit set on an ignored row"
+        assert np.all(g["loss"].numpy()[sel][~valid] == 0)
+        assert np.all(g["entropy"].numpy()[sel][~valid] == 0)
+    assert np.array_equal(ghit[sure], o["hit"][sure]), f"{label} hit differs on sure rows"
+
+
+def check_reduced(g: dict, o: dict, label: str = "") -> None:
+    rf = g["reduced_f32"].numpy().astype(np.float64)
+    ri = g["reduced_i64"].numpy()
+    for i, k in enumerate(("loss_sum", "loss_mean", "entropy_sum")):
+        ref = o[k]
+        if ref == 0.0:
+            assert rf[i] == 0.0, f"{label} {k} should be exactly 0, got {rf[i]}"
+        else:
+            assert abs(rf[i] - ref) <= TOL_REDUCED * abs(ref), f"{label} {k}: {rf[i]} vs {ref}"
+    assert int(ri[0]) == o["n_valid"], f"{label} n_valid {ri[0]} vs {o['n_valid']}"
+    assert int(ri[2]) == o["n_bad"], f"{label} n_bad {ri[2]} vs {o['n_bad']}"
+    assert int(ri[1]) == int(g["hit"].numpy().astype(np.int64).sum()), f"{label} n_correct != sum hit"
+
+
+def check_grad(a: np.ndarray, b: np.ndarray, name: str, label: str = "") -> None:
+    e = rel_fro(a, b)
+    assert e <= TOL_GRAD, f"{label} {name}: relative Frobenius error {e}"
+    zero_rows = np.all(b == 0, axis=tuple(range(1, b.ndim))) if b.ndim > 1 else (b == 0)
+    assert np.all(a[zero_rows] == 0), f"{label} {name}: nonzero where the oracle is exactly 0"

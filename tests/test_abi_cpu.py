@@ -1,0 +1,148 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/flce.h declares, its struct layout matches the binding, and argument
+errors are reported before anything is launched."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import linear_cross_entropy_fp32_amd as flce
+from linear_cross_entropy_fp32_amd import _binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "flce.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(flce_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = flce.lib()
+    declared = _declared_functions()
+    assert set(declared) == set(_binding.EXPORTED), declared
+    for name in declared:
+        assert hasattr(lib, name), f"{name} not exported"
+    out = subprocess.run(["nm", "-D", "--defined-only", _binding.LIB_PATH],
+                         capture_output=True, text=True, check=True).stdout
+    for name in declared:
+        assert re.search(rf"\bT {name}$", out, flags=re.M), f"{name} missing from dynamic symbols"
+
+
+def test_struct_layout_matches_header(tmp_path):
+    src = tmp_path / "layout.c"
+    fields = [f for f, _ in _binding.FlceProblem._fields_]
+    fmt = " ".join(["%zu"] * (len(fields) + 1))
+    offs = "".join(f", offsetof(flce_problem, {f})" for f in fields)
+    src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "flce.h"\n'
+                   f'int main(void) {{ printf("{fmt}\\n", sizeof(flce_problem){offs}); '
+                   'return 0; }\n')
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)],
+                   check=True)
+    vals = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True,
+                                           check=True).stdout.split()]
+    expect = [ctypes.sizeof(_binding.FlceProblem)] + [
+        getattr(_binding.FlceProblem, f).offset for f, _ in _binding.FlceProblem._fields_]
+    assert vals == expect
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(n_tokens=-1, hidden=64, vocab=10), -2),
+    (dict(n_tokens=4, hidden=12, vocab=10), -2),
+    (dict(n_tokens=4, hidden=0, vocab=10), -2),
+    (dict(n_tokens=4, hidden=64, vocab=0), -2),
+    (dict(n_tokens=1 << 20, hidden=1 << 12, vocab=10), -2),
+    (dict(n_tokens=4, hidden=64, vocab=10, weight_dtype=1), -3),
+    (dict(n_tokens=4, hidden=64, vocab=10, hidden_dtype=7), -3),
+    (dict(n_tokens=4, hidden=64, vocab=10, logit_scale=float("nan")), -7),
+    (dict(n_tokens=4, hidden=64, vocab=10, softcap=float("inf")), -7),
+    (dict(n_tokens=0, hidden=64, vocab=1), 0),
+    (dict(n_tokens=16384, hidden=4096, vocab=151936, hidden_dtype=1), 0),
+])
+def test_validate(kw, code):
+    p = flce.make_problem(**kw)
+    assert flce.flce_validate(p) == code
+    if code:
+        assert flce.flce_last_error()
+        with pytest.raises(flce.FlceError):
+            flce.flce_workspace_bytes(p)
+    else:
+        assert flce.flce_workspace_bytes(p) > 0
+
+
+def test_reserved_field_must_be_zero():
+    p = flce.make_problem(4, 64, 10)
+    p.reserved = 1
+    assert flce.flce_validate(p) == -7
+
+
+def test_workspace_is_bounded():
+    """The workspace never holds a tokens x vocab buffer: it is bounded by the
+    vocab-chunk of the backward plus per-token and per-split state."""
+    for n, h, v, dt in [(2048, 640, 262144, 0), (8192, 2048, 128256, 0),
+                        (16384, 1024, 151936, 0), (16384, 4096, 151936, 1)]:
+        ws = flce.flce_workspace_bytes(flce.make_problem(n, h, v, hidden_dtype=dt))
+        assert ws < 0.6 * n * v * 2 + 4 * n * h * 5, (n, h, v, ws)
+
+
+def _fake(addr):
+    return ctypes.c_void_p(addr)
+
+
+def test_entry_points_reject_before_launch():
+    """Null pointers, misalignment, a short workspace and bad modes return an
+    error code without touching the (fake, never dereferenced) pointers."""
+    lib = flce.lib()
+    p = flce.make_problem(8, 64, 100)
+    A = 0x100000
+    ok = [_fake(A)] * 2
+    args = lambda **o: dict(dict(h=_fake(A), w=_fake(A), b=None, t=_fake(A), loss=_fake(A),
+                                 lse=_fake(A), ent=_fake(A), hit=_fake(A), am=None,
+                                 rf=_fake(A), ri=_fake(A), ws=_fake(A), wsb=1 << 20,
+                                 s=None), **o)
+
+    def fwd(**o):
+        a = args(**o)
+        return lib.flce_forward(ctypes.byref(p), a["h"], a["w"], a["b"], a["t"], a["loss"],
+                                a["lse"], a["ent"], a["hit"], a["am"], a["rf"], a["ri"], a["ws"],
+                                a["wsb"], a["s"])
+
+    assert fwd(w=None) == -1
+    assert fwd(t=None) == -1
+    assert fwd(h=_fake(A + 8)) == -4
+    assert fwd(t=_fake(A + 4)) == -4
+    assert fwd(ws=_fake(A + 128)) == -4
+    assert fwd(wsb=16) == -5
+    assert "workspace" in flce.flce_last_error()
+
+    def bwd(mode=0, **o):
+        a = args(**o)
+        return lib.flce_backward(ctypes.byref(p), a["h"], a["w"], a["b"], a["t"], a["lse"],
+                                 a["ri"], mode, a["rf"], a["loss"], a["ent"], a.get("gb"),
+                                 a["ws"], a["wsb"], a["s"])
+
+    assert bwd(mode=3) == -7
+    assert bwd(mode=-1) == -7
+    assert bwd(w=None) == -1
+    assert bwd(wsb=16) == -5
+    # grad_bias without bias
+    a = args()
+    assert lib.flce_backward(ctypes.byref(p), a["h"], a["w"], None, a["t"], a["lse"], a["ri"],
+                             0, a["rf"], a["loss"], a["ent"], _fake(A), a["ws"], a["wsb"],
+                             None) == -7
+    del ok
+
+
+def test_binding_requires_targets_and_reduction():
+    import torch
+    h = torch.zeros(4, 64, dtype=torch.bfloat16)
+    w = torch.zeros(10, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        flce.linear_cross_entropy(h, w, None)
+    with pytest.raises(ValueError):
+        flce.linear_cross_entropy(h, w, torch.zeros(4, dtype=torch.int64), reduction="avg")

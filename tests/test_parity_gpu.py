@@ -1,0 +1,229 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle."""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import linear_cross_entropy_fp32_amd as flce
+from linear_cross_entropy_fp32_amd import synth
+from oracle import Problem, backward, final_logits, forward
+from tests.gpu_cases import (check_grad, check_reduced, check_tokens, prob_of, rel_fro, run_gpu,
+                             say, to_f64)
+
+pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    flce.lib()
+
+
+def _oracle_all(w, inp, mean_divisor=0.0):
+    h, wt, b = to_f64(inp.hidden), to_f64(inp.weight), to_f64(inp.bias)
+    t = inp.targets.numpy()
+    prob = prob_of(w, mean_divisor)
+    o = forward(h, wt, b, t, prob)
+    g = backward(h, wt, b, t, prob, w.reduction, inp.grad_out.numpy())
+    return o, g
+
+
+# Small shapes that span several tiles and leave ragged tails in N (tokens),
+# H (the K loop, in steps of 8) and V (vocabulary), one per feature combination.
+SMALL = [
+    synth.small_workload(300, 136, 1000, 11),
+    synth.small_workload(257, 64, 4099, 12, softcap=30.0, bias=True, logit_scale=0.5,
+                         reduction="sum"),
+    synth.small_workload(130, 264, 777, 13, hidden_dtype="f32", bias=True, reduction="none"),
+    synth.small_workload(333, 128, 2500, 14, logit_scale=0.0625, targets="zipf",
+                         reduction="sum"),
+    synth.small_workload(200, 256, 3001, 15, softcap=5.0, reduction="none", bias=True),
+    synth.small_workload(4100, 128, 40000, 16, reduction="mean"),       # two vocab chunks
+    synth.small_workload(96, 512, 1500, 17, hidden_dtype="f32", softcap=30.0),
+    synth.small_workload(64, 128, 1, 18),                                # V = 1
+    synth.small_workload(70, 64, 2, 19, bias=True),                      # V = 2
+]
+
+
+@pytest.mark.parametrize("w", SMALL, ids=lambda w: w.name)
+def test_small_parity(w):
+    say(f"[parity] {w.name}")
+    inp = synth.make_inputs(w)
+    g = run_gpu(w, inp)
+    o, og = _oracle_all(w, inp)
+    check_tokens(g, o, label=w.name)
+    check_reduced(g, o, label=w.name)
+    check_grad(g["grad_hidden"].numpy(), og["grad_hidden"], "grad_hidden", w.name)
+    check_grad(g["grad_weight"].numpy(), og["grad_weight"], "grad_weight", w.name)
+    if inp.bias is not None:
+        check_grad(g["grad_bias"].numpy(), og["grad_bias"], "grad_bias", w.name)
+
+
+def test_num_items_divisor():
+    w = synth.small_workload(150, 64, 900, 21)
+    say("[parity] num_items divisor")
+    inp = synth.make_inputs(w)
+    g = run_gpu(w, inp, mean_divisor=400.0)
+    o, og = _oracle_all(w, inp, mean_divisor=400.0)
+    check_reduced(g, o, "num_items")
+    check_grad(g["grad_weight"].numpy(), og["grad_weight"], "grad_weight", "num_items")
+
+
+def test_all_ignored_small_is_exactly_zero():
+    w = synth.small_workload(150, 128, 600, 22, targets="all_ignored", hidden_dtype="f32",
+                             bias=True, softcap=10.0)
+    say("[parity] all ignored (small)")
+    inp = synth.make_inputs(w)
+    g = run_gpu(w, inp)
+    assert np.all(g["loss"].numpy() == 0) and np.all(g["entropy"].numpy() == 0)
+    assert np.all(g["hit"].numpy() == 0)
+    assert g["reduced_f32"].numpy().tolist() == [0.0, 0.0, 0.0]
+    assert g["reduced_i64"].numpy().tolist() == [0, 0, 0]
+    for k in ("grad_hidden", "grad_weight", "grad_bias"):
+        assert torch.count_nonzero(g[k]).item() == 0, k
+
+
+def test_bad_targets_counted():
+    w = synth.small_workload(200, 64, 500, 23)
+    inp = synth.make_inputs(w)
+    inp.targets[5] = 500
+    inp.targets[7] = -3
+    inp.targets[9] = 10 ** 9
+    say("[parity] bad targets")
+    g = run_gpu(w, inp)
+    o, og = _oracle_all(w, inp)
+    assert o["n_bad"] == 3
+    check_tokens(g, o, label="bad")
+    check_reduced(g, o, label="bad")
+    check_grad(g["grad_hidden"].numpy(), og["grad_hidden"], "grad_hidden", "bad")
+
+
+def test_empty_batch():
+    say("[parity] N = 0")
+    dev = "cuda:0"
+    h = torch.zeros(0, 64, dtype=torch.bfloat16, device=dev)
+    w = torch.randn(300, 64, device=dev).to(torch.bfloat16)
+    t = torch.zeros(0, dtype=torch.int64, device=dev)
+    b = torch.randn(300, device=dev)
+    f = flce.flce_forward(h, w, t, b)
+    gh, gw, gb = flce.flce_backward(h, w, t, f["lse"], f["reduced_i64"], flce.FLCE_GRAD_MEAN,
+                                    torch.ones(1, device=dev), b)
+    torch.cuda.synchronize()
+    assert f["reduced_f32"].cpu().tolist() == [0.0, 0.0, 0.0]
+    assert f["reduced_i64"].cpu().tolist() == [0, 0, 0]
+    assert gh.numel() == 0 and torch.count_nonzero(gw).item() == 0
+    assert torch.count_nonzero(gb).item() == 0
+
+
+def test_deterministic_and_repeatable():
+    """Same inputs twice -> bitwise-identical outputs; the backward can be
+    called again (it keeps no state)."""
+    w = synth.small_workload(500, 192, 5000, 24, softcap=30.0, bias=True)
+    inp = synth.make_inputs(w)
+    say("[parity] determinism")
+    a = run_gpu(w, inp)
+    b = run_gpu(w, inp)
+    for k in ("loss", "lse", "entropy", "hit", "argmax", "reduced_f32", "reduced_i64",
+              "grad_hidden", "grad_weight", "grad_bias"):
+        assert torch.equal(a[k], b[k]), k
+
+
+@pytest.mark.parametrize("vocab", [32000, 150000, 200000])
+def test_argmax_targets_give_exact_accuracy(vocab):
+    """Targets set to the oracle's argmax of the final logits: every row whose
+    top-2 margin is at least 1e-2 must be a hit (the cce pull request's
+    accuracy check at V = 200000, 32000 and 150000)."""
+    w = synth.Workload(f"argmax_{vocab}", 256, 256, vocab, softcap=30.0, seed=31,
+                       ignore_every=0)
+    inp = synth.make_inputs(w)
+    z = final_logits(to_f64(inp.hidden), to_f64(inp.weight), None, prob_of(w))
+    inp.targets = torch.from_numpy(np.argmax(z, axis=1).astype(np.int64))
+    top2 = np.partition(z, vocab - 2, axis=1)[:, vocab - 2:]
+    sure = (top2[:, 1] - top2[:, 0]) >= 1e-2
+    say(f"[parity] argmax targets V={vocab}")
+    g = run_gpu(w, inp, backward=False)
+    assert np.all(g["hit"].numpy()[sure] == 1)
+    assert int(g["reduced_i64"][1]) == int(g["hit"].numpy().astype(np.int64).sum())
+
+
+def test_autograd_wrapper_matches_c_abi():
+    w = synth.small_workload(260, 128, 3000, 25, softcap=30.0, bias=True)
+    inp = synth.make_inputs(w)
+    dev = "cuda:0"
+    say("[parity] autograd wrapper")
+    ref = run_gpu(w, inp)
+    h = inp.hidden.to(dev).requires_grad_(True)
+    wt = inp.weight.to(dev).requires_grad_(True)
+    b = inp.bias.to(dev).requires_grad_(True)
+    t = inp.targets.to(dev)
+    loss, ent_sum, n_correct, n_valid = flce.linear_cross_entropy(h, wt, t, b, softcap=30.0)
+    loss.backward()
+    torch.cuda.synchronize()
+    assert loss.item() == ref["reduced_f32"][1].item()
+    assert ent_sum.item() == ref["reduced_f32"][2].item()
+    assert n_correct.item() == ref["reduced_i64"][1].item()
+    assert n_valid.item() == ref["reduced_i64"][0].item()
+    assert torch.equal(b.grad.cpu(), ref["grad_bias"])
+    assert torch.equal(h.grad.cpu(), ref["grad_hidden"].to(torch.bfloat16))
+    assert torch.equal(wt.grad.cpu(), ref["grad_weight"].to(torch.bfloat16))
+    # per-token reduction with weights: grad of sum(g * loss)
+    h.grad = None
+    lt, *_ = flce.linear_cross_entropy(h, wt, t, b, softcap=30.0, reduction="none")
+    gw8 = torch.rand(lt.shape, device=dev)
+    (lt * gw8).sum().backward()
+    o = forward(to_f64(inp.hidden), to_f64(inp.weight), to_f64(inp.bias), inp.targets.numpy(),
+                Problem(softcap=30.0))
+    assert np.abs(lt.detach().cpu().numpy() - o["loss"]).max() <= 2e-3
+    og = backward(to_f64(inp.hidden), to_f64(inp.weight), to_f64(inp.bias), inp.targets.numpy(),
+                  Problem(softcap=30.0), "none", gw8.cpu().numpy().astype(np.float64))
+    assert rel_fro(h.grad.float().cpu().numpy(), og["grad_hidden"]) <= 1e-2
+
+
+# ------------------------------------------------------- full-size workloads
+
+FULL = ["tiny", "huge_vocab", "bias_none", "zipf_sum", "fp32_hidden", "fp32_hidden_all_ignored"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_fullsize_against_stored_oracle(name):
+    """The full workloads, in the launch configuration the bench times,
+    against oracle values written by tests/golden/make_fullsize_golden.py:
+    every row's loss / entropy / lse / argmax / hit, the reductions, sampled
+    grad_hidden rows and sampled grad_weight / grad_bias rows.  The identity
+    sum_v <gw_v, W_v> = sum_n <gh_n, h_n> is checked over the whole outputs."""
+    path = os.path.join(GOLDEN, f"fullsize_{name}.npz")
+    if not os.path.exists(path):
+        pytest.skip(f"{path} not generated")
+    gold = np.load(path, allow_pickle=False)
+    w = synth.WORKLOADS[name]
+    say(f"[parity] full size {name}: drawing inputs")
+    inp = synth.make_inputs(w)
+    assert synth.input_checksum(inp) == str(gold["checksum"]), "input generator drifted"
+    say(f"[parity] full size {name}: running")
+    g = run_gpu(w, inp)
+    o = {k: gold[k] for k in ("loss", "lse", "entropy", "argmax", "hit", "margin")}
+    t = inp.targets.numpy()
+    o["valid"] = (t >= 0) & (t < w.vocab)
+    for k in ("loss_sum", "loss_mean", "entropy_sum"):
+        o[k] = float(gold[k])
+    for k in ("n_valid", "n_correct", "n_bad"):
+        o[k] = int(gold[k])
+    check_tokens(g, o, label=name)
+    check_reduced(g, o, label=name)
+    rows, vrows = gold["rows"], gold["vocab_rows"]
+    check_grad(g["grad_hidden"].numpy()[rows], gold["grad_hidden_rows"], "grad_hidden rows", name)
+    check_grad(g["grad_weight"].numpy()[vrows], gold["grad_weight_rows"], "grad_weight rows", name)
+    if inp.bias is not None:
+        check_grad(g["grad_bias"].numpy()[vrows], gold["grad_bias_rows"], "grad_bias rows", name)
+    if o["n_valid"] == 0:
+        for k in ("grad_hidden", "grad_weight"):
+            assert torch.count_nonzero(g[k]).item() == 0, k
+        return
+    lhs = float((g["grad_weight"].double() * inp.weight.double()).sum())
+    rhs = float((g["grad_hidden"].double() * inp.hidden.double()).sum())
+    scale = float(g["grad_weight"].double().norm() * inp.weight.double().norm())
+    assert abs(lhs - rhs) <= 1e-2 * scale, (lhs, rhs, scale)
