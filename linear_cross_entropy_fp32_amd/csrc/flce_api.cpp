@@ -29,7 +29,7 @@ constexpr int64_t kMaxHidden = int64_t(1) << 20;
 constexpr int64_t kMaxElems = int64_t(1) << 31;      // N*H and V*H stay int32-indexable per row
 constexpr size_t kAlign = 256;
 constexpr int64_t kTargetWgs = 2048;                 // ~8 workgroups per CU
-constexpr int64_t kDzChunkBytes = int64_t(1) << 28;  // vocab chunk of the staged backward
+constexpr int64_t kDzChunkBytes = int64_t(1) << 28;  // bf16 dz of one backward vocab chunk
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline int64_t rup(int64_t a, int64_t b) { return cdiv(a, b) * b; }
@@ -37,8 +37,9 @@ inline size_t aup(size_t a) { return (a + kAlign - 1) / kAlign * kAlign; }
 
 struct Plan {
   int n_tok_tiles, n_voc_tiles, n_splits, tiles_per_split, fin_blocks;
-  int64_t vc;            // vocab chunk width of the backward (multiple of the tile)
+  int64_t vc;            // vocab chunk width of the backward (multiple of the logit tile)
   int n_chunks;
+  int dz_tiles_per_wg;   // vocab tiles streamed by one dz workgroup
   int gh_splits;         // split-K of the grad_hidden contraction
   int64_t gh_kps;
   size_t off_hsplit, off_part, off_bsums, off_dz, off_ghpart;
@@ -80,7 +81,7 @@ Plan make_plan(const flce_problem* p) {
   splits = std::max<int64_t>(1, std::min<int64_t>(splits, pl.n_voc_tiles));
   pl.tiles_per_split = (int)cdiv(pl.n_voc_tiles, splits);
   pl.n_splits = (int)cdiv(pl.n_voc_tiles, pl.tiles_per_split);
-  pl.fin_blocks = (int)cdiv(n, 256);
+  pl.fin_blocks = (int)cdiv(n, 32);
 
   // backward: vocab chunks of about kDzChunkBytes of bf16 dz
   int64_t vc = n > 0 ? (kDzChunkBytes / (2 * n)) / kLogitTileV * kLogitTileV : rup(v, kLogitTileV);
@@ -88,12 +89,15 @@ Plan make_plan(const flce_problem* p) {
   vc = std::min<int64_t>(vc, rup(v, kLogitTileV));
   pl.vc = vc;
   pl.n_chunks = (int)cdiv(v, vc);
-  const int64_t gh_tiles = cdiv(n, kGemmTileM) * cdiv(h, kGemmTileN);
-  const int64_t kloop = std::min<int64_t>(vc, v);
-  int64_t ghs = gh_tiles > 0 ? cdiv(1024, gh_tiles) : 1;
-  ghs = std::max<int64_t>(1, std::min<int64_t>(ghs, cdiv(kloop, 256)));
-  pl.gh_kps = rup(cdiv(kloop, ghs), 64);
-  pl.gh_splits = (int)cdiv(kloop, pl.gh_kps);
+  const int64_t chunk_tiles = vc / kLogitTileV;
+  pl.dz_tiles_per_wg = (int)std::max<int64_t>(1, chunk_tiles * pl.n_tok_tiles / kTargetWgs);
+  // grad_hidden split: give its workgroups about the K depth of the
+  // grad_weight ones (N), at most 8 partial slots
+  const int64_t width = std::min<int64_t>(vc, v);
+  int64_t ghs = n > 0 ? cdiv(width, std::max<int64_t>(n, 1024)) : 1;
+  ghs = std::max<int64_t>(1, std::min<int64_t>(ghs, 8));
+  pl.gh_kps = rup(cdiv(width, ghs), kSliceK);
+  pl.gh_splits = (int)cdiv(width, pl.gh_kps);
 
   size_t off = 0;
   pl.off_hsplit = off;
@@ -214,7 +218,11 @@ int flce_forward(const flce_problem* p, const void* hidden, const void* weight,
     a.tiles_per_split = pl.tiles_per_split;
     a.n_voc_tiles = pl.n_voc_tiles;
     a.part = part;
-    if ((rc = hip_check(launch_fwd_stats(a, p->softcap > 0, s), "fwd_stats"))) return rc;
+    // softcapped logits lie below c: with 2c*log2(e) <= 120 the sums can use
+    // the fixed reference c (no running max) without underflowing fp32
+    const bool fixed_ref = p->softcap > 0 && 2.0 * p->softcap * 1.4426950408889634 <= 120.0;
+    if ((rc = hip_check(launch_fwd_stats(a, p->softcap > 0, fixed_ref, s), "fwd_stats")))
+      return rc;
   }
   FinalArgs f{};
   f.part = part;
@@ -303,61 +311,36 @@ int flce_backward(const flce_problem* p, const void* hidden, const void* weight,
   d.ignore_index = p->ignore_index;
   logit_consts(p, d.kx, d.c1, d.c2);
   d.n_tok_tiles = pl.n_tok_tiles;
+  d.tiles_per_wg = pl.dz_tiles_per_wg;
   d.dz = dz;
   d.ldz = pl.vc;
+
+  ContractArgs g{};
+  g.dz = dz;
+  g.ldz = pl.vc;
+  g.h = h0;
+  g.n = (int)n;
+  g.hdim = (int)h;
+  g.gh_splits = pl.gh_splits;
+  g.gh_kps = (int)pl.gh_kps;
+  g.gh_m_tiles = (int)cdiv(n, kGemmTileM);
+  g.n_tiles = (int)cdiv(h, kGemmTileN);
+  g.gh_wgs = pl.gh_splits * g.gh_m_tiles * g.n_tiles;
+  g.gh = pl.gh_splits > 1 ? ghpart : grad_hidden;
 
   for (int c = 0; c < pl.n_chunks; ++c) {
     const int64_t c0 = int64_t(c) * pl.vc;
     const int64_t width = std::min<int64_t>(pl.vc, v - c0);
     d.c0 = (int)c0;
-    const int tiles = (int)cdiv(width, kLogitTileV);
-    if ((rc = hip_check(launch_bwd_dz(d, tiles, p->softcap > 0, s), "bwd_dz"))) return rc;
+    d.chunk_tiles = (int)cdiv(width, kLogitTileV);
+    if ((rc = hip_check(launch_bwd_dz(d, p->softcap > 0, s), "bwd_dz"))) return rc;
 
-    // grad_hidden[n, :] (+)= sum_v dz[n, v] W[c0 + v, :]
-    GemmArgs g{};
-    g.a_ptr = dz;
-    g.lda = pl.vc;
-    g.a_row_bound = (int)n;
-    g.a_k_bound = (int)pl.vc;
-    g.b_ptr = static_cast<const uint16_t*>(weight) + c0 * h;
-    g.ldb = h;
-    g.b_row_bound = (int)h;
-    g.b_k_bound = (int)width;
-    g.n_tiles = (int)cdiv(h, kGemmTileN);
-    g.k_len = (int)width;
-    g.k_per_split = (int)pl.gh_kps;
-    g.c = pl.gh_splits > 1 ? ghpart : grad_hidden;
-    g.ldc = h;
-    g.c_split_stride = n * h;
-    g.m_store = (int)n;
-    g.n_store = (int)h;
-    g.accumulate = c > 0;
-    if ((rc = hip_check(launch_gemm_store(g, (int)cdiv(n, kGemmTileM), pl.gh_splits, true, s),
-                        "gemm_grad_hidden")))
-      return rc;
-
-    // grad_weight[c0 + v, :] = sum_n dz[n, v] h[n, :]
-    GemmArgs gw{};
-    gw.a_ptr = dz;
-    gw.lda = pl.vc;
-    gw.a_row_bound = (int)pl.vc;
-    gw.a_k_bound = (int)n;
-    gw.b_ptr = h0;
-    gw.ldb = h;
-    gw.b_row_bound = (int)h;
-    gw.b_k_bound = (int)n;
-    gw.n_tiles = (int)cdiv(h, kGemmTileN);
-    gw.k_len = (int)n;
-    gw.k_per_split = (int)rup(n, 64);
-    gw.c = grad_weight + c0 * h;
-    gw.ldc = h;
-    gw.c_split_stride = 0;
-    gw.m_store = (int)width;
-    gw.n_store = (int)h;
-    gw.accumulate = 0;
-    if ((rc = hip_check(launch_gemm_store(gw, (int)cdiv(width, kGemmTileM), 1, false, s),
-                        "gemm_grad_weight")))
-      return rc;
+    g.w = static_cast<const uint16_t*>(weight) + c0 * h;
+    g.width = (int)width;
+    g.gh_accumulate = c > 0;
+    g.gw = grad_weight + c0 * h;
+    const int gw_wgs = (int)(cdiv(width, kGemmTileM) * g.n_tiles);
+    if ((rc = hip_check(launch_contract(g, gw_wgs, s), "contract"))) return rc;
 
     if (grad_bias &&
         (rc = hip_check(launch_colsum(dz, pl.vc, (int)n, (int)width, grad_bias + c0, s), "colsum")))

@@ -5,14 +5,13 @@
 
 namespace flce {
 
-// Tile shape of the logit-tile kernels (forward stats, backward dz) and of
-// the contraction kernels: TM x TN blocks of 32x32 per wave, 2x2 waves.
-constexpr int kTM = 2, kTN = 2;     // 128 vocab x 128 tokens
-constexpr int kGM = 2, kGN = 2;     // 128 x 128 output tile
-constexpr int kLogitTileV = 64 * kTM;
-constexpr int kLogitTileN = 64 * kTN;
-constexpr int kGemmTileM = 64 * kGM;
-constexpr int kGemmTileN = 64 * kGN;
+// Logit tiles (forward stats, backward dz): 128 vocabulary rows x 256 tokens.
+constexpr int kLogitTileV = 128;
+constexpr int kLogitTileN = 256;
+// Contraction tiles (grad_hidden, grad_weight): 256 x 128 outputs.
+constexpr int kGemmTileM = 256;
+constexpr int kGemmTileN = 128;
+constexpr int kSliceK = 32;   // K values per pipeline slice
 
 // Online softmax state of one token over a range of vocabulary rows, in base-2
 // units (u = z * log2 e): running max m, S = sum 2^(u-m), T = sum 2^(u-m) u,
@@ -68,34 +67,35 @@ struct DzArgs {
   int64_t ignore_index;
   float kx, c1, c2;
   int c0;                // first vocab row of the chunk
+  int chunk_tiles;       // vocab tiles in the chunk
+  int tiles_per_wg;      // vocab tiles streamed by one workgroup
   int n_tok_tiles;
   uint16_t* dz;          // [N, ldz] bf16 chunk buffer
   int64_t ldz;
 };
 
-struct GemmArgs {
-  const uint16_t* a_ptr;
-  int64_t lda;
-  int a_row_bound, a_k_bound;
-  const uint16_t* b_ptr;
-  int64_t ldb;
-  int b_row_bound, b_k_bound;
-  int n_tiles;
-  int k_len, k_per_split;
-  float* c;
-  int64_t ldc, c_split_stride;
-  int m_store, n_store;
-  int accumulate;
+// One launch per vocab chunk computes both contractions of the chunk's dz:
+// workgroups [0, gh_wgs) the grad_hidden split-K partials, the rest the
+// grad_weight rows of the chunk.
+struct ContractArgs {
+  const uint16_t* dz;    // [N, ldz] bf16
+  int64_t ldz;
+  const uint16_t* w;     // lm_head rows of the chunk: w + c0 * H
+  const uint16_t* h;     // [N, H] bf16 (the high part for fp32 hidden)
+  int n, hdim, width;    // tokens, hidden, vocab rows in the chunk
+  int gh_wgs, gh_splits, gh_kps, gh_m_tiles, n_tiles;
+  float* gh;             // [gh_splits, N, H] partials, or grad_hidden when gh_splits == 1
+  int gh_accumulate;
+  float* gw;             // grad_weight + c0 * H
 };
 
 hipError_t launch_split_hidden(const float* h, uint16_t* hi, uint16_t* lo, int64_t count,
                                hipStream_t s);
-hipError_t launch_fwd_stats(const FwdArgs& a, bool cap, hipStream_t s);
+hipError_t launch_fwd_stats(const FwdArgs& a, bool cap, bool fixed_ref, hipStream_t s);
 hipError_t launch_fwd_finalize(const FinalArgs& a, int nblocks, float mean_divisor,
                                float* red_f32, int64_t* red_i64, hipStream_t s);
-hipError_t launch_bwd_dz(const DzArgs& a, int n_voc_tiles_chunk, bool cap, hipStream_t s);
-hipError_t launch_gemm_store(const GemmArgs& a, int m_tiles, int splits, bool a_kmaj,
-                             hipStream_t s);
+hipError_t launch_bwd_dz(const DzArgs& a, bool cap, hipStream_t s);
+hipError_t launch_contract(const ContractArgs& a, int gw_wgs, hipStream_t s);
 hipError_t launch_sum_partials(const float* part, int nsplit, int64_t stride, float* out,
                                int64_t count, hipStream_t s);
 hipError_t launch_colsum(const uint16_t* dz, int64_t ldz, int n_tok, int width, float* out,

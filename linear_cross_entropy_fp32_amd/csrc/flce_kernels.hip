@@ -1,27 +1,35 @@
 // HIP kernels of the fused linear cross-entropy for gfx950.
 //
 // The method (TRL pull request "Add loss_type="cce", a fused linear
-// cross-entropy loaded from the Hub", sections "What it supports" and the
-// review's "Correctness" facts): the logits are the hidden x lm_head product
+// cross-entropy loaded from the Hub", "What it supports" and the review's
+// "Correctness" facts): the logits are the hidden x lm_head product
 // accumulated in fp32, plus an fp32 bias, times logit_scale, then softcapped;
 // the loss, the entropy (lse - sum p z) and the argmax all come from one pass
 // over those logits, which are never stored.
 //
 // Units: inside the kernels a final logit z is carried as u = z * log2(e), so
 // every exponential is one v_exp_f32 (2^x).  The forward keeps, per token, an
-// online state (running max m, S = sum 2^(u-m), T = sum 2^(u-m) u, best value,
+// online state (reference m, S = sum 2^(u-m), T = sum 2^(u-m) u, best value,
 // best index, target value), all in base-2 units.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include "flce_internal.h"
-#include "tile_gemm.h"
+#include "tile_engine.h"
 
 namespace flce {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegInf = -__builtin_huge_valf();
+// Value given to logits of rows past the vocabulary in the last tile: below
+// every real logit, and 2^(it - m) is exactly 0 with 0 * it finite.
+constexpr float kMasked = -3.0e38f;
+
+using LogitTile = Tile<kLogitTileV, kLogitTileN, kSliceK, true, true>;      // 128 x 256
+using GhTile = Tile<kGemmTileM, kGemmTileN, kSliceK, true, false>;          // dz . W
+using GwTile = Tile<kGemmTileM, kGemmTileN, kSliceK, false, false>;         // dz^T . h
+constexpr int kColumns = LogitTile::TN;      // token columns per lane
 
 // ------------------------------------------------------------------ helpers
 
@@ -36,7 +44,14 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-// Merge two online states.  Sums are rescaled to the larger running max; the
+// Row offset, inside a wave's 64 vocabulary rows, of value q (0..31) of a
+// lane's token column (q = 16 * block + accumulator register), not counting
+// the +4 of the lane's half-wave.
+__host__ __device__ constexpr int q_row(int q) {
+  return (q >> 4) * 32 + ((q & 15) >> 2) * 8 + (q & 3);
+}
+
+// Merge two online states.  Sums are rescaled to the larger reference; the
 // argmax keeps the larger value and, on a tie, the lower vocabulary index; the
 // target value is finite in at most one of the two states.
 __device__ __forceinline__ PartState merge_state(PartState a, const PartState& b) {
@@ -77,7 +92,7 @@ __device__ __forceinline__ PartState shfl_xor_state(const PartState& s, int mask
 // u = x * kx + bk with kx = s*log2e, bk = s*log2e*b.  With softcap c:
 // c*tanh(y) = c - 2c / (1 + e^(2y)), y = s*(x+b)/c, so with kx = 2*s*log2e/c,
 // bk = kx*b: e = 2^(x*kx + bk), r = 1/(1+e), u = c*log2e - 2c*log2e*r.
-// `r` is returned for the backward's softcap slope 1 - tanh^2 = 4 r (1 - r).
+// `r` is also the backward's softcap slope: 1 - tanh^2 = 4 r (1 - r).
 template <bool CAP>
 __device__ __forceinline__ float final_u(float x, float kx, float bk, float c1, float c2,
                                          float& r) {
@@ -88,6 +103,25 @@ __device__ __forceinline__ float final_u(float x, float kx, float bk, float c1, 
   } else {
     r = 0.f;
     return fmaf(x, kx, bk);
+  }
+}
+
+// Bias terms (b * kx) of the 32 rows a lane holds in a wave's 64-row slab;
+// rows past the vocabulary read zero through the buffer bound.
+template <bool BIAS>
+__device__ __forceinline__ void load_bias(const float* bias, int v, int vw, float kx,
+                                          float (&bk)[32]) {
+  if constexpr (BIAS) {
+    const int half = (threadIdx.x & 63) >> 5;
+    const __amdgpu_buffer_rsrc_t rs = tile_rsrc(bias, (int64_t)v * 4);
+#pragma unroll
+    for (int q = 0; q < 32; ++q) {
+      const uint32_t off = (uint32_t)(vw + q_row(q) + half * 4) * 4;
+      bk[q] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0)) * kx;
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < 32; ++q) bk[q] = 0.f;
   }
 }
 
@@ -113,144 +147,186 @@ __global__ void split_hidden_kernel(const float* __restrict__ h, uint16_t* __res
 }
 
 // ------------------------------------------------------------- forward: K1
+// Fold one token column (32 values in a lane) of a finished logit tile into
+// that token's state.  `val` holds the values in place of the accumulators.
+//
+// FIXED (softcap with 2c*log2e <= 120): every final logit is below c, so the
+// sums use the fixed reference m = c*log2e and need no running max: the
+// value kept is d = u - c*log2e = -2c*log2e*r.  Otherwise the two-pass online
+// fold: tile max first, then the exponentials against the new reference.
+template <bool CAP, bool FIXED>
+__device__ __forceinline__ void fold_column(float (&val)[32], PartState& st, int tgt, int vw,
+                                            int half) {
+  float mt = val[0];
+#pragma unroll
+  for (int q = 1; q < 32; ++q) mt = fmaxf(mt, val[q]);
+  // argmax: the first (lowest-row) position holding the tile maximum
+  if (mt > st.bu) {
+    int row = 0;
+#pragma unroll
+    for (int q = 31; q >= 0; --q)
+      if (val[q] == mt) row = q_row(q);
+    st.bu = mt;
+    st.bi = vw + half * 4 + row;
+  }
+  // target value: only in lanes whose target row is one of their rows
+  {
+    const int rel = tgt - vw - half * 4;
+    if (rel >= 0 && rel < 64 && (rel & 4) == 0) {
+#pragma unroll
+      for (int q = 0; q < 32; ++q)
+        if (q_row(q) == rel) st.zt = val[q];
+    }
+  }
+  float s4[4] = {0.f, 0.f, 0.f, 0.f}, t4[4] = {0.f, 0.f, 0.f, 0.f};
+  if constexpr (FIXED) {
+#pragma unroll
+    for (int q = 0; q < 32; ++q) {
+      const float p = fast_exp2(val[q]);
+      s4[q & 3] += p;
+      t4[q & 3] = fmaf(p, val[q], t4[q & 3]);
+    }
+    st.s += (s4[0] + s4[1]) + (s4[2] + s4[3]);
+    st.t += (t4[0] + t4[1]) + (t4[2] + t4[3]);
+  } else {
+    // a lane that has only seen rows past the vocabulary keeps an empty state
+    const float mn = fmaxf(st.m, mt);
+    if (mn > kMasked) {
+      const float alpha = fast_exp2(st.m - mn);
+#pragma unroll
+      for (int q = 0; q < 32; ++q) {
+        const float p = fast_exp2(val[q] - mn);
+        s4[q & 3] += p;
+        t4[q & 3] = fmaf(p, val[q], t4[q & 3]);
+      }
+      st.s = fmaf(st.s, alpha, (s4[0] + s4[1]) + (s4[2] + s4[3]));
+      st.t = fmaf(st.t, alpha, (t4[0] + t4[1]) + (t4[2] + t4[3]));
+      st.m = mn;
+    }
+  }
+}
+
+template <bool CAP, bool FIXED, bool BIAS>
+struct FwdEpilogue {
+  const FwdArgs& a;
+  PartState (&st)[kColumns];
+  const int (&tgt)[kColumns];
+  int vt_begin, wm, half;
+
+  __device__ __forceinline__ void operator()(int t, LogitTile& T) {
+    const int v0 = (vt_begin + t) * kLogitTileV;
+    const int vw = v0 + wm * (kLogitTileV / 2);
+    const bool tail = v0 + kLogitTileV > a.v;
+    float bk[32];
+    load_bias<BIAS>(a.bias, a.v, vw, a.kx, bk);
+#pragma unroll
+    for (int j = 0; j < kColumns; ++j) {
+      float val[32];
+#pragma unroll
+      for (int q = 0; q < 32; ++q) {
+        const float x = T.acc[q >> 4][j][q & 15];
+        if constexpr (FIXED) {
+          const float e = fast_exp2(fmaf(x, a.kx, bk[q]));
+          val[q] = -a.c2 * fast_rcp(e + 1.0f);
+        } else {
+          float r;
+          val[q] = final_u<CAP>(x, a.kx, bk[q], a.c1, a.c2, r);
+        }
+      }
+      if (tail) {
+#pragma unroll
+        for (int q = 0; q < 32; ++q)
+          if (vw + half * 4 + q_row(q) >= a.v) val[q] = kMasked;
+      }
+      fold_column<CAP, FIXED>(val, st[j], tgt[j], vw, half);
+    }
+  }
+};
+
 // One workgroup = one token tile x one contiguous range ("split") of vocab
-// tiles.  For each vocab tile the logit tile is computed with MFMA and folded
-// into the per-token online state held in registers; at the end of the split
-// the states of the two half-waves and of the two waves sharing a token are
-// merged and written as one partial state per (split, token).
-template <int TM, int TN, bool CAP>
-__global__ void __launch_bounds__(kThreads)
+// tiles, streamed through the tile engine; each finished logit tile is folded
+// into the per-token states held in registers.  At the end of the split the
+// states of the two half-waves and of the two waves sharing a token are merged
+// and written as one partial state per (split, token).
+template <bool CAP, bool FIXED, bool BIAS>
+__global__ void __launch_bounds__(kThreads, 2)
 fwd_stats_kernel(const FwdArgs a) {
-  using T = Tile<TM, TN, true, true>;
-  __shared__ __attribute__((aligned(16))) char lds[T::kLdsBytes];
+  __shared__ __attribute__((aligned(16))) char lds[LogitTile::kLdsBytes];
   const int bid = xcd_remap(blockIdx.x, gridDim.x);
   const int tt = bid % a.n_tok_tiles, sp = bid / a.n_tok_tiles;
-  const int n0 = tt * T::BN;
+  const int n0 = tt * kLogitTileN;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave & 1, wn = wave >> 1;
   const int half = lane >> 5;
 
-  int tgt[TN];
-  PartState st[TN];
+  int tgt[kColumns];
+  PartState st[kColumns];
 #pragma unroll
-  for (int j = 0; j < TN; ++j) {
-    const int n = n0 + wn * (T::BN / 2) + j * 32 + (lane & 31);
-    int64_t t = (n < a.n) ? a.tgt[n] : -1;
-    tgt[j] = (t >= 0 && t < a.v) ? (int)t : -1;
-    st[j] = PartState{kNegInf, 0.f, 0.f, kNegInf, kNegInf, 0x7fffffff};
+  for (int j = 0; j < kColumns; ++j) {
+    const int n = n0 + wn * (kLogitTileN / 2) + j * 32 + (lane & 31);
+    const int64_t t = (n < a.n) ? a.tgt[n] : -1;
+    tgt[j] = (t >= 0 && t < a.v) ? (int)t : -(1 << 30);
+    st[j] = PartState{FIXED ? 0.f : kNegInf, 0.f, 0.f, kNegInf, kNegInf, 0x7fffffff};
   }
-
-  const Operand opB0{a.h0, a.hdim, n0, a.n, a.hdim};
-  const Operand opB1{a.h1, a.hdim, n0, a.n, a.hdim};
   const int vt_begin = sp * a.tiles_per_split;
-  const int vt_end = min(a.n_voc_tiles, vt_begin + a.tiles_per_split);
-  T tile;
-  for (int vt = vt_begin; vt < vt_end; ++vt) {
-    const int v0 = vt * T::BM;
-    const Operand opA{a.w, a.hdim, v0, a.v, a.hdim};
-    tile.zero();
-    tile.run(lds, opA, opB0, opB1, a.h1 != nullptr, 0, a.hdim);
+  const int ntiles = min(a.n_voc_tiles, vt_begin + a.tiles_per_split) - vt_begin;
+  const Operand opA{a.w, a.hdim, vt_begin * kLogitTileV, a.v, a.hdim};
+  const Operand opB0{a.h0, a.hdim, n0, a.n, a.hdim};
+  const Operand opB1{a.h1 ? a.h1 : a.h0, a.hdim, n0, a.n, a.hdim};
+  FwdEpilogue<CAP, FIXED, BIAS> epi{a, st, tgt, vt_begin, wm, half};
+  LogitTile T;
+  T.run_stream(lds, opA, opB0, opB1, a.h1 != nullptr, a.hdim, ntiles, epi);
 
-    const int vw = v0 + wm * (T::BM / 2);   // first vocab row of this wave
-    const bool tail = (v0 + T::BM > a.v);
-    // bias term per accumulator row, shared by the TN token columns
-    float bk[TM][16];
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int v = vw + i * 32 + acc_row(r, lane);
-        float b = 0.f;
-        if (a.bias && v < a.v) b = a.bias[v];
-        bk[i][r] = b * a.kx;
-      }
-#pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      float u[TM * 16];
-      float mt = kNegInf;
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float rr;
-          float x = final_u<CAP>(tile.acc[i][j][r], a.kx, bk[i][r], a.c1, a.c2, rr);
-          if (tail && vw + i * 32 + acc_row(r, lane) >= a.v) x = kNegInf;
-          u[i * 16 + r] = x;
-          mt = fmaxf(mt, x);
-        }
-      // argmax: the first (lowest-index) position holding the tile maximum
-      if (mt > st[j].bu) {
-        int idx = 0x7fffffff;
-#pragma unroll
-        for (int q = TM * 16 - 1; q >= 0; --q)
-          if (u[q] == mt) idx = vw + (q >> 4) * 32 + acc_row(q & 15, lane);
-        st[j].bu = mt;
-        st[j].bi = idx;
-      }
-      // target logit: only lanes whose target row falls in this wave's rows
-      {
-        const int rel = tgt[j] - vw;
-        if (rel >= 0 && rel < TM * 32 && ((rel >> 2) & 1) == half) {
-#pragma unroll
-          for (int q = 0; q < TM * 16; ++q)
-            if ((q >> 4) * 32 + acc_row(q & 15, lane) == rel) st[j].zt = u[q];
-        }
-      }
-      const float mn = fmaxf(st[j].m, mt);
-      if (mn != kNegInf) {
-        const float alpha = fast_exp2(st[j].m - mn);
-        float s4[4] = {0.f, 0.f, 0.f, 0.f}, t4[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int q = 0; q < TM * 16; ++q) {
-          const float p = fast_exp2(u[q] - mn);
-          s4[q & 3] += p;
-          if (tail) {
-            t4[q & 3] += (u[q] != kNegInf) ? p * u[q] : 0.f;
-          } else {
-            t4[q & 3] = fmaf(p, u[q], t4[q & 3]);
-          }
-        }
-        st[j].s = fmaf(st[j].s, alpha, (s4[0] + s4[1]) + (s4[2] + s4[3]));
-        st[j].t = fmaf(st[j].t, alpha, (t4[0] + t4[1]) + (t4[2] + t4[3]));
-        st[j].m = mn;
-      }
+  for (int j = 0; j < kColumns; ++j) {
+    if constexpr (FIXED) {
+      // back from d = u - c*log2e to the reference m = c*log2e
+      st[j].m = a.c1;
+      st[j].t = fmaf(a.c1, st[j].s, st[j].t);
+      st[j].bu += a.c1;
+      st[j].zt += a.c1;
     }
+    st[j] = merge_state(st[j], shfl_xor_state(st[j], 32));
   }
-
-  // merge the two half-waves (same token, interleaved vocab rows)
-#pragma unroll
-  for (int j = 0; j < TN; ++j) st[j] = merge_state(st[j], shfl_xor_state(st[j], 32));
-  // merge the two waves that share a token column, then write the partial
   PartState* sh = reinterpret_cast<PartState*>(lds);
   if (wm == 1 && half == 0) {
 #pragma unroll
-    for (int j = 0; j < TN; ++j) sh[(wn * TN + j) * 32 + lane] = st[j];
+    for (int j = 0; j < kColumns; ++j) sh[(wn * kColumns + j) * 32 + lane] = st[j];
   }
   __syncthreads();
   if (wm == 0 && half == 0) {
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const PartState o = merge_state(st[j], sh[(wn * TN + j) * 32 + lane]);
-      const int n = n0 + wn * (T::BN / 2) + j * 32 + lane;
+    for (int j = 0; j < kColumns; ++j) {
+      const PartState o = merge_state(st[j], sh[(wn * kColumns + j) * 32 + lane]);
+      const int n = n0 + wn * (kLogitTileN / 2) + j * 32 + lane;
       if (n < a.n) a.part[(int64_t)sp * a.n + n] = o;
     }
   }
 }
 
 // ------------------------------------------------------- forward: K2 merge
-// One thread per token merges the partial states of all splits in split
-// order, then derives lse, loss, entropy, argmax and hit; each block writes
-// fixed-order partial sums for the reductions.
+// 8 threads per token merge interleaved subsets of the splits, then a fixed
+// xor tree merges the 8 partial states; the first thread of each token
+// derives lse, loss, entropy, argmax and hit.  Each block writes fixed-order
+// partial sums for the reductions.
+constexpr int kMergeLanes = 8;
+constexpr int kFinalTokens = 256 / kMergeLanes;
+
 __global__ void __launch_bounds__(256)
 fwd_finalize_kernel(const FinalArgs a) {
-  const int n = blockIdx.x * blockDim.x + threadIdx.x;
+  const int sub = threadIdx.x % kMergeLanes;
+  const int n = blockIdx.x * kFinalTokens + threadIdx.x / kMergeLanes;
+  PartState st{kNegInf, 0.f, 0.f, kNegInf, kNegInf, 0x7fffffff};
+  if (n < a.n)
+    for (int s = sub; s < a.n_splits; s += kMergeLanes)
+      st = merge_state(st, a.part[(int64_t)s * a.n + n]);
+#pragma unroll
+  for (int m = 1; m < kMergeLanes; m <<= 1) st = merge_state(st, shfl_xor_state(st, m));
+
   double l_sum = 0.0, e_sum = 0.0;
   int nv = 0, nc = 0, nb = 0;
-  if (n < a.n) {
-    PartState st = a.part[n];
-    for (int s = 1; s < a.n_splits; ++s) st = merge_state(st, a.part[(int64_t)s * a.n + n]);
+  if (n < a.n && sub == 0) {
     const float lse2 = st.m + log2f(st.s);
-    const float lse = lse2 * kLn2;
     const int64_t t = a.tgt[n];
     const bool ignored = (t == a.ignore_index);
     const bool valid = !ignored && t >= 0 && t < a.v;
@@ -262,7 +338,7 @@ fwd_finalize_kernel(const FinalArgs a) {
       hit = (st.bi == (int)t) ? 1 : 0;
     }
     a.loss[n] = loss;
-    a.lse[n] = lse;
+    a.lse[n] = lse2 * kLn2;
     a.entropy[n] = ent;
     a.hit[n] = hit;
     if (a.argmax) a.argmax[n] = st.bi;
@@ -272,7 +348,6 @@ fwd_finalize_kernel(const FinalArgs a) {
     nc = hit;
     nb = (!ignored && !valid);
   }
-  // fixed-shape tree reduction inside the block
   __shared__ double sl[256], se[256];
   __shared__ int sv[256], sc[256], sb[256];
   sl[threadIdx.x] = l_sum;
@@ -291,10 +366,7 @@ fwd_finalize_kernel(const FinalArgs a) {
     }
     __syncthreads();
   }
-  if (threadIdx.x == 0) {
-    BlockSums bs{sl[0], se[0], sv[0], sc[0], sb[0], 0};
-    a.block_sums[blockIdx.x] = bs;
-  }
+  if (threadIdx.x == 0) a.block_sums[blockIdx.x] = BlockSums{sl[0], se[0], sv[0], sc[0], sb[0], 0};
 }
 
 __global__ void fwd_reduce_kernel(const BlockSums* __restrict__ bs, int nblocks,
@@ -320,8 +392,8 @@ __global__ void fwd_reduce_kernel(const BlockSums* __restrict__ bs, int nblocks,
 }
 
 // --------------------------------------------------- backward: dz recompute
-// Recomputes one logit tile and writes the fp32 chain-ruled gradient w.r.t.
-// the raw product, rounded to bf16, into a vocab chunk of the workspace:
+// Recomputes logit tiles and writes the fp32 chain-ruled gradient w.r.t. the
+// raw product, rounded to bf16, into a vocabulary chunk of the workspace:
 // dz[n, v] = g_n * s * (p - [v == t_n]) * (softcap ? 1 - tanh^2 : 1).
 __device__ __forceinline__ float row_grad(const DzArgs& a, int n, int64_t t) {
   if (n >= a.n) return 0.f;
@@ -339,129 +411,160 @@ __device__ __forceinline__ float row_grad(const DzArgs& a, int n, int64_t t) {
   return g * a.scale;
 }
 
-template <int TM, int TN, bool CAP>
-__global__ void __launch_bounds__(kThreads)
+template <bool CAP, bool BIAS>
+struct DzEpilogue {
+  const DzArgs& a;
+  const float (&gs)[kColumns];     // g_n * s (times 4 with softcap: the slope is 4 r (1-r))
+  const float (&nl)[kColumns];     // -lse_n in base-2 units
+  const int (&tgt)[kColumns];
+  const int (&nrow)[kColumns];
+  int vt_begin, wm, half;
+
+  __device__ __forceinline__ void operator()(int t, LogitTile& T) {
+    const int v0 = a.c0 + (vt_begin + t) * kLogitTileV;
+    const int vw = v0 + wm * (kLogitTileV / 2);
+    const bool tail = v0 + kLogitTileV > a.v;
+    float bk[32];
+    load_bias<BIAS>(a.bias, a.v, vw, a.kx, bk);
+#pragma unroll
+    for (int j = 0; j < kColumns; ++j) {
+      float d[32];
+#pragma unroll
+      for (int q = 0; q < 32; ++q) {
+        const float x = T.acc[q >> 4][j][q & 15];
+        if constexpr (CAP) {
+          const float e = fast_exp2(fmaf(x, a.kx, bk[q]));
+          const float r = fast_rcp(e + 1.0f);
+          const float p = fast_exp2(fmaf(-a.c2, r, a.c1 + nl[j]));
+          d[q] = p * (fmaf(-r, r, r) * gs[j]);       // g s p (1 - tanh^2), gs carries the 4
+        } else {
+          d[q] = fast_exp2(fmaf(x, a.kx, bk[q] + nl[j])) * gs[j];
+        }
+      }
+      // one-hot term, only in lanes whose target row is one of their rows
+      {
+        const int rel = tgt[j] - vw - half * 4;
+        if (rel >= 0 && rel < 64 && (rel & 4) == 0) {
+#pragma unroll
+          for (int q = 0; q < 32; ++q)
+            if (q_row(q) == rel) {
+              if constexpr (CAP) {
+                const float e = fast_exp2(fmaf(T.acc[q >> 4][j][q & 15], a.kx, bk[q]));
+                const float r = fast_rcp(e + 1.0f);
+                d[q] -= fmaf(-r, r, r) * gs[j];
+              } else {
+                d[q] -= gs[j];
+              }
+            }
+        }
+      }
+      if (tail) {
+#pragma unroll
+        for (int q = 0; q < 32; ++q)
+          if (vw + half * 4 + q_row(q) >= a.v) d[q] = 0.f;
+      }
+      if (nrow[j] >= 0) {
+        uint16_t* row = a.dz + (int64_t)nrow[j] * a.ldz + (vw - a.c0) + half * 4;
+#pragma unroll
+        for (int g4 = 0; g4 < 8; ++g4) {
+          u32x2 pk;
+          pk[0] = pack_bf16x2(d[g4 * 4 + 0], d[g4 * 4 + 1]);
+          pk[1] = pack_bf16x2(d[g4 * 4 + 2], d[g4 * 4 + 3]);
+          *reinterpret_cast<u32x2*>(row + q_row(g4 * 4)) = pk;
+        }
+      }
+    }
+  }
+};
+
+template <bool CAP, bool BIAS>
+__global__ void __launch_bounds__(kThreads, 2)
 bwd_dz_kernel(const DzArgs a) {
-  using T = Tile<TM, TN, true, true>;
-  __shared__ __attribute__((aligned(16))) char lds[T::kLdsBytes];
+  __shared__ __attribute__((aligned(16))) char lds[LogitTile::kLdsBytes];
   const int bid = xcd_remap(blockIdx.x, gridDim.x);
-  const int tt = bid % a.n_tok_tiles, vt = bid / a.n_tok_tiles;
-  const int n0 = tt * T::BN;
-  const int v0 = a.c0 + vt * T::BM;
+  const int tt = bid % a.n_tok_tiles, grp = bid / a.n_tok_tiles;
+  const int n0 = tt * kLogitTileN;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave & 1, wn = wave >> 1;
   const int half = lane >> 5;
 
-  const Operand opA{a.w, a.hdim, v0, a.v, a.hdim};
-  const Operand opB0{a.h0, a.hdim, n0, a.n, a.hdim};
-  const Operand opB1{a.h1, a.hdim, n0, a.n, a.hdim};
-  T tile;
-  tile.zero();
-  tile.run(lds, opA, opB0, opB1, a.h1 != nullptr, 0, a.hdim);
-
-  const int vw = v0 + wm * (T::BM / 2);
-  const bool tail = (v0 + T::BM > a.v);
-  float bk[TM][16];
+  float gs[kColumns], nl[kColumns];
+  int tgt[kColumns], nrow[kColumns];
 #pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int v = vw + i * 32 + acc_row(r, lane);
-      float b = 0.f;
-      if (a.bias && v < a.v) b = a.bias[v];
-      bk[i][r] = b * a.kx;
-    }
-#pragma unroll
-  for (int j = 0; j < TN; ++j) {
-    const int n = n0 + wn * (T::BN / 2) + j * 32 + (lane & 31);
+  for (int j = 0; j < kColumns; ++j) {
+    const int n = n0 + wn * (kLogitTileN / 2) + j * 32 + (lane & 31);
     const int64_t t = (n < a.n) ? a.tgt[n] : -1;
-    const float gs = row_grad(a, n, t);
-    const float lse2 = (n < a.n) ? a.lse[n] * kLog2e : 0.f;
-    float d[TM * 16];
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float rr;
-        const float u = final_u<CAP>(tile.acc[i][j][r], a.kx, bk[i][r], a.c1, a.c2, rr);
-        float p = fast_exp2(u - lse2);
-        if constexpr (CAP) p *= 4.0f * rr * (1.0f - rr);
-        d[i * 16 + r] = p;
-      }
-    // one-hot term, only where the target row is one of this lane's rows
-    const int rel = (int)t - vw;
-    if (t >= 0 && rel >= 0 && rel < TM * 32 && ((rel >> 2) & 1) == half) {
-#pragma unroll
-      for (int q = 0; q < TM * 16; ++q)
-        if ((q >> 4) * 32 + acc_row(q & 15, lane) == rel) {
-          float rr;
-          const float u = final_u<CAP>(tile.acc[q >> 4][j][q & 15], a.kx, bk[q >> 4][q & 15],
-                                       a.c1, a.c2, rr);
-          (void)u;
-          d[q] -= CAP ? 4.0f * rr * (1.0f - rr) : 1.0f;
-        }
-    }
-    if (n < a.n) {
-      uint16_t* row = a.dz + (int64_t)n * a.ldz;
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const int vl = vw + i * 32 + g4 * 8 + half * 4;   // first of 4 consecutive rows
-          float x0 = d[i * 16 + g4 * 4 + 0] * gs, x1 = d[i * 16 + g4 * 4 + 1] * gs;
-          float x2 = d[i * 16 + g4 * 4 + 2] * gs, x3 = d[i * 16 + g4 * 4 + 3] * gs;
-          if (tail) {
-            if (vl + 0 >= a.v) x0 = 0.f;
-            if (vl + 1 >= a.v) x1 = 0.f;
-            if (vl + 2 >= a.v) x2 = 0.f;
-            if (vl + 3 >= a.v) x3 = 0.f;
-          }
-          u32x2 pk;
-          pk[0] = pack_bf16x2(x0, x1);
-          pk[1] = pack_bf16x2(x2, x3);
-          *reinterpret_cast<u32x2*>(row + (vl - a.c0)) = pk;
-        }
-    }
+    gs[j] = row_grad(a, n, t) * (CAP ? 4.0f : 1.0f);
+    nl[j] = (n < a.n) ? -a.lse[n] * kLog2e : 0.f;
+    tgt[j] = (t >= 0 && t < a.v) ? (int)t : -(1 << 30);
+    nrow[j] = (n < a.n) ? n : -1;
   }
+  const int vt_begin = grp * a.tiles_per_wg;
+  const int ntiles = min(a.chunk_tiles, vt_begin + a.tiles_per_wg) - vt_begin;
+  const Operand opA{a.w, a.hdim, a.c0 + vt_begin * kLogitTileV, a.v, a.hdim};
+  const Operand opB0{a.h0, a.hdim, n0, a.n, a.hdim};
+  const Operand opB1{a.h1 ? a.h1 : a.h0, a.hdim, n0, a.n, a.hdim};
+  DzEpilogue<CAP, BIAS> epi{a, gs, nl, tgt, nrow, vt_begin, wm, half};
+  LogitTile T;
+  T.run_stream(lds, opA, opB0, opB1, a.h1 != nullptr, a.hdim, ntiles, epi);
 }
 
 // ------------------------------------------- contractions over a dz chunk
-// C[m, n] (+)= sum_k A(m, k) B(n, k) for one tile; grid.y splits K, each
-// split owning its own slice of C (partials reduced later in fixed order).
-template <int TM, int TN, bool A_KMAJ, bool B_KMAJ>
-__global__ void __launch_bounds__(kThreads)
-gemm_store_kernel(const GemmArgs a) {
-  using T = Tile<TM, TN, A_KMAJ, B_KMAJ>;
-  __shared__ __attribute__((aligned(16))) char lds[T::kLdsBytes];
-  const int bid = xcd_remap(blockIdx.x, gridDim.x);
-  const int tn = bid % a.n_tiles, tm = bid / a.n_tiles;
-  const int m0 = tm * T::BM, n0 = tn * T::BN;
-  const int kb = blockIdx.y * a.k_per_split;
-  const int ke = min(a.k_len, kb + a.k_per_split);
-  Operand opA{a.a_ptr, a.lda, m0, a.a_row_bound, a.a_k_bound};
-  Operand opB{a.b_ptr, a.ldb, n0, a.b_row_bound, a.b_k_bound};
-  T tile;
-  tile.zero();
-  tile.run(lds, opA, opB, opB, false, kb, ke);
-
+// Workgroups [0, gh_wgs): grad_hidden (+)= dz[:, chunk] . W[chunk, :], split
+// over the chunk's vocabulary into gh_splits partial slots.  The rest:
+// grad_weight[chunk, :] = dz[:, chunk]^T . h.
+template <class T>
+__device__ __forceinline__ void store_tile(const T& tile, float* c, int64_t ldc, int m0, int n0,
+                                           int m_bound, int n_bound, bool accumulate) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave & 1, wn = wave >> 1;
-  float* c = a.c + (int64_t)blockIdx.y * a.c_split_stride;
 #pragma unroll
-  for (int i = 0; i < TM; ++i)
+  for (int i = 0; i < T::TM; ++i)
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const int n = n0 + wn * (T::BN / 2) + j * 32 + (lane & 31);
-      if (n >= a.n_store) continue;
+    for (int j = 0; j < T::TN; ++j) {
+      const int n = n0 + wn * (T::kBN / 2) + j * 32 + (lane & 31);
+      if (n >= n_bound) continue;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int m = m0 + wm * (T::BM / 2) + i * 32 + acc_row(r, lane);
-        if (m < a.m_store) {
-          float* p = c + (int64_t)m * a.ldc + n;
-          *p = a.accumulate ? (*p + tile.acc[i][j][r]) : tile.acc[i][j][r];
+        const int m = m0 + wm * (T::kBM / 2) + i * 32 + acc_row(r, lane);
+        if (m < m_bound) {
+          float* p = c + (int64_t)m * ldc + n;
+          *p = accumulate ? (*p + tile.acc[i][j][r]) : tile.acc[i][j][r];
         }
       }
     }
+}
+
+constexpr int kContractLds =
+    GhTile::kLdsBytes > GwTile::kLdsBytes ? GhTile::kLdsBytes : GwTile::kLdsBytes;
+
+__global__ void __launch_bounds__(kThreads, 2)
+contract_kernel(const ContractArgs a) {
+  __shared__ __attribute__((aligned(16))) char lds[kContractLds];
+  const int width8 = (a.width + 7) & ~7;
+  if ((int)blockIdx.x < a.gh_wgs) {
+    const int per = a.gh_m_tiles * a.n_tiles;
+    const int z = blockIdx.x / per, rem = blockIdx.x % per;
+    const int tm = rem / a.n_tiles, tn = rem % a.n_tiles;
+    const int kb = z * a.gh_kps;
+    const int ke = min(a.width, kb + a.gh_kps);
+    const Operand opA{a.dz, a.ldz, tm * kGemmTileM, a.n, width8};
+    const Operand opB{a.w, a.hdim, tn * kGemmTileN, a.hdim, a.width};
+    GhTile T;
+    T.zero();
+    T.run(lds, opA, opB, opB, false, kb, ke);
+    store_tile(T, a.gh + (int64_t)z * a.n * a.hdim, a.hdim, tm * kGemmTileM, tn * kGemmTileN,
+               a.n, a.hdim, a.gh_accumulate != 0);
+  } else {
+    const int b = blockIdx.x - a.gh_wgs;
+    const int tm = b / a.n_tiles, tn = b % a.n_tiles;
+    const Operand opA{a.dz, a.ldz, tm * kGemmTileM, width8, a.n};
+    const Operand opB{a.h, a.hdim, tn * kGemmTileN, a.hdim, a.n};
+    GwTile T;
+    T.zero();
+    T.run(lds, opA, opB, opB, false, 0, a.n);
+    store_tile(T, a.gw, a.hdim, tm * kGemmTileM, tn * kGemmTileN, a.width, a.hdim, false);
+  }
 }
 
 // out[i] = sum_z part[z][i], z in order.
@@ -507,14 +610,19 @@ hipError_t launch_split_hidden(const float* h, uint16_t* hi, uint16_t* lo, int64
   return hipGetLastError();
 }
 
-hipError_t launch_fwd_stats(const FwdArgs& a, bool cap, hipStream_t s) {
+hipError_t launch_fwd_stats(const FwdArgs& a, bool cap, bool fixed_ref, hipStream_t s) {
   const unsigned grid = (unsigned)(a.n_tok_tiles * a.n_splits);
   if (grid == 0) return hipSuccess;
-  if (cap) {
-    fwd_stats_kernel<kTM, kTN, true><<<grid, kThreads, 0, s>>>(a);
+  const bool bias = a.bias != nullptr;
+#define FLCE_FWD(C, F, B) fwd_stats_kernel<C, F, B><<<grid, kThreads, 0, s>>>(a)
+  if (cap && fixed_ref) {
+    if (bias) FLCE_FWD(true, true, true); else FLCE_FWD(true, true, false);
+  } else if (cap) {
+    if (bias) FLCE_FWD(true, false, true); else FLCE_FWD(true, false, false);
   } else {
-    fwd_stats_kernel<kTM, kTN, false><<<grid, kThreads, 0, s>>>(a);
+    if (bias) FLCE_FWD(false, false, true); else FLCE_FWD(false, false, false);
   }
+#undef FLCE_FWD
   return hipGetLastError();
 }
 
@@ -525,26 +633,25 @@ hipError_t launch_fwd_finalize(const FinalArgs& a, int nblocks, float mean_divis
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_dz(const DzArgs& a, int n_voc_tiles_chunk, bool cap, hipStream_t s) {
-  const unsigned grid = (unsigned)(a.n_tok_tiles * n_voc_tiles_chunk);
+hipError_t launch_bwd_dz(const DzArgs& a, bool cap, hipStream_t s) {
+  const int groups = (a.chunk_tiles + a.tiles_per_wg - 1) / a.tiles_per_wg;
+  const unsigned grid = (unsigned)(a.n_tok_tiles * groups);
   if (grid == 0) return hipSuccess;
+  const bool bias = a.bias != nullptr;
   if (cap) {
-    bwd_dz_kernel<kTM, kTN, true><<<grid, kThreads, 0, s>>>(a);
+    if (bias) bwd_dz_kernel<true, true><<<grid, kThreads, 0, s>>>(a);
+    else bwd_dz_kernel<true, false><<<grid, kThreads, 0, s>>>(a);
   } else {
-    bwd_dz_kernel<kTM, kTN, false><<<grid, kThreads, 0, s>>>(a);
+    if (bias) bwd_dz_kernel<false, true><<<grid, kThreads, 0, s>>>(a);
+    else bwd_dz_kernel<false, false><<<grid, kThreads, 0, s>>>(a);
   }
   return hipGetLastError();
 }
 
-hipError_t launch_gemm_store(const GemmArgs& a, int m_tiles, int splits, bool a_kmaj,
-                             hipStream_t s) {
-  dim3 grid((unsigned)(m_tiles * a.n_tiles), (unsigned)splits);
-  if (grid.x == 0 || grid.y == 0) return hipSuccess;
-  if (a_kmaj) {
-    gemm_store_kernel<kGM, kGN, true, false><<<grid, kThreads, 0, s>>>(a);
-  } else {
-    gemm_store_kernel<kGM, kGN, false, false><<<grid, kThreads, 0, s>>>(a);
-  }
+hipError_t launch_contract(const ContractArgs& a, int gw_wgs, hipStream_t s) {
+  const unsigned grid = (unsigned)(a.gh_wgs + gw_wgs);
+  if (grid == 0) return hipSuccess;
+  contract_kernel<<<grid, kThreads, 0, s>>>(a);
   return hipGetLastError();
 }
 
