@@ -32,6 +32,8 @@ def parse():
     ap.add_argument("--workload", default="huge_vocab")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB (HBM counter scale)")
     return ap.parse_args()
 
 
@@ -73,6 +75,18 @@ def main() -> int:
               "the path's sharding is described in DESIGN.md", file=sys.stderr)
         return 2
     import torch
+
+    if args.copy_calibration_mib:
+        # a plain copy of known size: rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE on
+        # this run gives the counters' scale for algorithmic byte counts
+        n = args.copy_calibration_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(max(1, args.steps)):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "copies": max(1, args.steps)}), flush=True)
+        return 0
 
     import linear_cross_entropy_fp32_amd as flce
     from linear_cross_entropy_fp32_amd import _binding, synth

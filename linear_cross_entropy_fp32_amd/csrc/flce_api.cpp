@@ -29,6 +29,7 @@ constexpr int64_t kMaxHidden = int64_t(1) << 20;
 constexpr int64_t kMaxElems = int64_t(1) << 31;      // N*H and V*H stay int32-indexable per row
 constexpr size_t kAlign = 256;
 constexpr int64_t kTargetWgs = 2048;                 // ~8 workgroups per CU
+constexpr int64_t kDzWgs = 512;                      // dz workgroups per chunk: one round at two per CU
 constexpr int64_t kDzChunkBytes = int64_t(1) << 28;  // bf16 dz of one backward vocab chunk
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -90,12 +91,13 @@ Plan make_plan(const flce_problem* p) {
   pl.vc = vc;
   pl.n_chunks = (int)cdiv(v, vc);
   const int64_t chunk_tiles = vc / kLogitTileV;
-  pl.dz_tiles_per_wg = (int)std::max<int64_t>(1, chunk_tiles * pl.n_tok_tiles / kTargetWgs);
-  // grad_hidden split: give its workgroups about the K depth of the
-  // grad_weight ones (N), at most 8 partial slots
+  pl.dz_tiles_per_wg = (int)std::max<int64_t>(1, chunk_tiles * pl.n_tok_tiles / kDzWgs);
+  // grad_hidden split: its workgroups get twice the K depth of the
+  // grad_weight ones (N); the launch interleaves the two kinds so every XCD
+  // gets the same mix, and fewer splits mean fewer partial slots to update
   const int64_t width = std::min<int64_t>(vc, v);
-  int64_t ghs = n > 0 ? cdiv(width, std::max<int64_t>(n, 1024)) : 1;
-  ghs = std::max<int64_t>(1, std::min<int64_t>(ghs, 8));
+  int64_t ghs = n > 0 ? cdiv(width, std::max<int64_t>(2 * n, 1024)) : 1;
+  ghs = std::max<int64_t>(1, std::min<int64_t>(ghs, 16));
   pl.gh_kps = rup(cdiv(width, ghs), kSliceK);
   pl.gh_splits = (int)cdiv(width, pl.gh_kps);
 
@@ -325,7 +327,6 @@ int flce_backward(const flce_problem* p, const void* hidden, const void* weight,
   g.gh_kps = (int)pl.gh_kps;
   g.gh_m_tiles = (int)cdiv(n, kGemmTileM);
   g.n_tiles = (int)cdiv(h, kGemmTileN);
-  g.gh_wgs = pl.gh_splits * g.gh_m_tiles * g.n_tiles;
   g.gh = pl.gh_splits > 1 ? ghpart : grad_hidden;
 
   for (int c = 0; c < pl.n_chunks; ++c) {
@@ -339,8 +340,9 @@ int flce_backward(const flce_problem* p, const void* hidden, const void* weight,
     g.width = (int)width;
     g.gh_accumulate = c > 0;
     g.gw = grad_weight + c0 * h;
-    const int gw_wgs = (int)(cdiv(width, kGemmTileM) * g.n_tiles);
-    if ((rc = hip_check(launch_contract(g, gw_wgs, s), "contract"))) return rc;
+    g.gw_m_tiles = (int)cdiv(width, kGemmTileM);
+    g.gw_rows_per_unit = (int)cdiv(g.gw_m_tiles, pl.gh_splits);
+    if ((rc = hip_check(launch_contract(g, s), "contract"))) return rc;
 
     if (grad_bias &&
         (rc = hip_check(launch_colsum(dz, pl.vc, (int)n, (int)width, grad_bias + c0, s), "colsum")))

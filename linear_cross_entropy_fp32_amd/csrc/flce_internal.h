@@ -75,15 +75,15 @@ struct DzArgs {
 };
 
 // One launch per vocab chunk computes both contractions of the chunk's dz:
-// workgroups [0, gh_wgs) the grad_hidden split-K partials, the rest the
-// grad_weight rows of the chunk.
+// the grad_hidden split-K partials and the grad_weight rows of the chunk.
 struct ContractArgs {
   const uint16_t* dz;    // [N, ldz] bf16
   int64_t ldz;
   const uint16_t* w;     // lm_head rows of the chunk: w + c0 * H
   const uint16_t* h;     // [N, H] bf16 (the high part for fp32 hidden)
   int n, hdim, width;    // tokens, hidden, vocab rows in the chunk
-  int gh_wgs, gh_splits, gh_kps, gh_m_tiles, n_tiles;
+  int gh_splits, gh_kps, gh_m_tiles, n_tiles;
+  int gw_m_tiles, gw_rows_per_unit;   // unit u: gh split u, then gw tile rows of the unit
   float* gh;             // [gh_splits, N, H] partials, or grad_hidden when gh_splits == 1
   int gh_accumulate;
   float* gw;             // grad_weight + c0 * H
@@ -95,7 +95,7 @@ hipError_t launch_fwd_stats(const FwdArgs& a, bool cap, bool fixed_ref, hipStrea
 hipError_t launch_fwd_finalize(const FinalArgs& a, int nblocks, float mean_divisor,
                                float* red_f32, int64_t* red_i64, hipStream_t s);
 hipError_t launch_bwd_dz(const DzArgs& a, bool cap, hipStream_t s);
-hipError_t launch_contract(const ContractArgs& a, int gw_wgs, hipStream_t s);
+hipError_t launch_contract(const ContractArgs& a, hipStream_t s);
 hipError_t launch_sum_partials(const float* part, int nsplit, int64_t stride, float* out,
                                int64_t count, hipStream_t s);
 hipError_t launch_colsum(const uint16_t* dz, int64_t ldz, int n_tok, int width, float* out,

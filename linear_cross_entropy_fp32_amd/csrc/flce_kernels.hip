@@ -542,9 +542,17 @@ __global__ void __launch_bounds__(kThreads, 2)
 contract_kernel(const ContractArgs a) {
   __shared__ __attribute__((aligned(16))) char lds[kContractLds];
   const int width8 = (a.width + 7) & ~7;
-  if ((int)blockIdx.x < a.gh_wgs) {
-    const int per = a.gh_m_tiles * a.n_tiles;
-    const int z = blockIdx.x / per, rem = blockIdx.x % per;
+  // The grid is cut into units, one per grad_hidden split: the split's tiles
+  // (which share its dz columns and lm_head rows) followed by a run of
+  // grad_weight tile rows (the H tiles of one dz slab adjacent).  Every unit
+  // carries about the same work, and the remap keeps consecutive ids on one
+  // XCD, so each XCD gets whole units and its L2 serves their shared operands.
+  const int bid = xcd_remap(blockIdx.x, gridDim.x);
+  const int gh_per_unit = a.gh_m_tiles * a.n_tiles;
+  const int unit_size = gh_per_unit + a.gw_rows_per_unit * a.n_tiles;
+  const int unit = bid / unit_size, off = bid % unit_size;
+  if (off < gh_per_unit) {
+    const int z = unit, rem = off;
     const int tm = rem / a.n_tiles, tn = rem % a.n_tiles;
     const int kb = z * a.gh_kps;
     const int ke = min(a.width, kb + a.gh_kps);
@@ -556,8 +564,9 @@ contract_kernel(const ContractArgs a) {
     store_tile(T, a.gh + (int64_t)z * a.n * a.hdim, a.hdim, tm * kGemmTileM, tn * kGemmTileN,
                a.n, a.hdim, a.gh_accumulate != 0);
   } else {
-    const int b = blockIdx.x - a.gh_wgs;
-    const int tm = b / a.n_tiles, tn = b % a.n_tiles;
+    const int b = off - gh_per_unit;
+    const int tm = unit * a.gw_rows_per_unit + b / a.n_tiles, tn = b % a.n_tiles;
+    if (tm >= a.gw_m_tiles) return;
     const Operand opA{a.dz, a.ldz, tm * kGemmTileM, width8, a.n};
     const Operand opB{a.h, a.hdim, tn * kGemmTileN, a.hdim, a.n};
     GwTile T;
@@ -648,8 +657,9 @@ hipError_t launch_bwd_dz(const DzArgs& a, bool cap, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_contract(const ContractArgs& a, int gw_wgs, hipStream_t s) {
-  const unsigned grid = (unsigned)(a.gh_wgs + gw_wgs);
+hipError_t launch_contract(const ContractArgs& a, hipStream_t s) {
+  const unsigned grid = (unsigned)(a.gh_splits *
+                                   (a.gh_m_tiles * a.n_tiles + a.gw_rows_per_unit * a.n_tiles));
   if (grid == 0) return hipSuccess;
   contract_kernel<<<grid, kThreads, 0, s>>>(a);
   return hipGetLastError();
