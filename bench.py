@@ -68,6 +68,53 @@ def cpu_baseline(w, inp, budget_s: float) -> dict:
                       f"(float64 numpy), {dt:.1f} s"}
 
 
+def _hip_runtime():
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipEventCreate.argtypes = [ctypes.c_void_p]
+    hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                        ctypes.c_void_p]
+    hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    return hip
+
+
+def _hip_ok(rc: int) -> None:
+    if rc != 0:
+        raise RuntimeError(f"HIP runtime call failed with code {rc}")
+
+
+def _chunks_per_backward(prob) -> int:
+    """Upper bound on contraction launches per backward: one per vocab chunk of
+    at most 2^28 bytes of bf16 dz (the library's own planning is finer)."""
+    n = max(1, prob.n_tokens)
+    rows = max(128, ((1 << 28) // (2 * n)) // 128 * 128)
+    return max(1, -(-prob.vocab // rows))
+
+
+def _source_digest() -> str:
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "linear_cross_entropy_fp32_amd", "csrc", "*"))):
+        with open(f, "rb") as fh:
+            h.update(os.path.basename(f).encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def _committed_traffic(workload: str, kernel: str):
+    """HBM bytes per launch of `kernel` from the committed counter summary
+    (rocprofv3 FETCH_SIZE and WRITE_SIZE, copy-calibrated), or None when the
+    kernels have changed since those counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+    try:
+        with open(path) as fh:
+            rec = json.load(fh)
+    except OSError:
+        return None
+    if rec.get("source_digest") != _source_digest():
+        return None
+    return rec.get("bytes_per_launch")
+
+
 def main() -> int:
     args = parse()
     if args.gpus != 1:
@@ -133,10 +180,20 @@ def main() -> int:
         fwd()
         bwd()
     torch.cuda.synchronize()
+
+    # HIP events for the dominant kernel's launches, recorded by the library on
+    # the launch stream (flce_set_timing_events) over the whole timed region
+    hip = _hip_runtime()
+    n_chunks = _chunks_per_backward(prob)
+    n_pairs = args.steps * n_chunks
+    evs = (ctypes.c_void_p * (2 * n_pairs))()
+    for i in range(2 * n_pairs):
+        _hip_ok(hip.hipEventCreate(ctypes.byref(evs, i * ctypes.sizeof(ctypes.c_void_p))))
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
            torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
+    flce.flce_set_timing_events(_binding.FLCE_KERNEL_CONTRACT, evs, n_pairs)
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
     start.record(stream)
@@ -149,15 +206,29 @@ def main() -> int:
     stop.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall
+    recorded = flce.flce_set_timing_events(_binding.FLCE_KERNEL_CONTRACT, None, 0)
+    kern_ms = []
+    for i in range(recorded):
+        ms_i = ctypes.c_float(0.0)
+        _hip_ok(hip.hipEventElapsedTime(ctypes.byref(ms_i), ctypes.c_void_p(evs[2 * i]),
+                                        ctypes.c_void_p(evs[2 * i + 1])))
+        kern_ms.append(ms_i.value)
+    for i in range(2 * n_pairs):
+        hip.hipEventDestroy(ctypes.c_void_p(evs[i]))
     total_ms = start.elapsed_time(stop)
     fwd_ms = sum(e0.elapsed_time(e1) for e0, e1, _ in ev) / args.steps
     bwd_ms = sum(e1.elapsed_time(e2) for _, e1, e2 in ev) / args.steps
     ms = total_ms / args.steps
     flops = 8.0 * n * hd * v
     tflops = flops / (ms * 1e-3) / 1e12
-    # dominant kernel: the forward call is one logit-tile kernel plus a merge
-    # of a few microseconds; its algorithmic work is 2*N*H*V flops per launch.
-    fwd_tflops = 2.0 * n * hd * v / (fwd_ms * 1e-3) / 1e12
+    # dominant kernel: the backward contraction (grad_hidden and grad_weight of
+    # one vocabulary chunk per launch); over a step its launches do 4*N*H*V
+    # flops of algorithmic work
+    launches = max(1, len(kern_ms))
+    kern_avg = sum(kern_ms) / launches if kern_ms else float("nan")
+    per_step_ms = kern_avg * launches / args.steps
+    kern_tflops = 4.0 * n * hd * v / (per_step_ms * 1e-3) / 1e12
+    traffic = _committed_traffic(w.name, "contract_kernel")
     out = {
         "metric": METRIC, "value": n / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
@@ -168,9 +239,10 @@ def main() -> int:
                    "softcap": w.softcap, "reduction": w.reduction},
         "tflops": tflops, "pct_bf16_peak": 100.0 * tflops / PEAK_BF16_TFLOPS,
         "fwd_ms": fwd_ms, "bwd_ms": bwd_ms, "wall_s": wall,
-        "roofline": {"bound": "mfma", "kernel": "fwd_stats_kernel", "achieved": fwd_tflops,
+        "roofline": {"bound": "mfma", "kernel": "contract_kernel", "achieved": kern_tflops,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": fwd_tflops / PEAK_BF16_TFLOPS, "traffic": None},
+                     "frac": kern_tflops / PEAK_BF16_TFLOPS, "traffic": traffic,
+                     "launch_ms": kern_avg, "launches_per_step": launches / args.steps},
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds)

@@ -23,7 +23,8 @@
  *   - `stream` is a hipStream_t (passed as void*); all work is enqueued on it,
  *     nothing is synchronised and no host<->device copy is made;
  *   - the caller owns every buffer, including the workspace; the library
- *     allocates nothing and keeps no state between calls, so calls are
+ *     allocates nothing and keeps no state between calls (apart from the
+ *     optional per-thread benchmark timing hook below), so calls are
  *     re-entrant and the backward may be called any number of times;
  *   - outputs are overwritten, never accumulated into;
  *   - on error nothing is launched, a negative FLCE_ERR_* code is returned and
@@ -107,6 +108,19 @@ int flce_backward(const flce_problem* p, const void* hidden, const void* weight,
                   const int64_t* reduced_i64, int grad_mode, const float* grad_out,
                   float* grad_hidden, float* grad_weight, float* grad_bias, void* workspace,
                   size_t workspace_bytes, void* stream);
+
+/* Benchmark instrumentation (not part of the loss API).  While set, every
+ * launch of `kernel` made by this thread is bracketed by hipEventRecord of
+ * events[2i] before and events[2i+1] after it, on the launch stream, for
+ * i = 0 .. n_pairs-1; later launches are not recorded.  `events` holds
+ * hipEvent_t handles owned by the caller and must stay valid while set.
+ * kernel: FLCE_KERNEL_FWD_STATS, FLCE_KERNEL_BWD_DZ or FLCE_KERNEL_CONTRACT.
+ * n_pairs = 0 clears it.  Returns the number of pairs recorded under the
+ * previous setting (>= 0) or FLCE_ERR_ARG. */
+#define FLCE_KERNEL_FWD_STATS 0
+#define FLCE_KERNEL_BWD_DZ 1
+#define FLCE_KERNEL_CONTRACT 2
+int flce_set_timing_events(int kernel, void* const* events, int n_pairs);
 
 /* Description of the last error on this thread ("" if none). */
 const char* flce_last_error(void);

@@ -7,5 +7,6 @@ raises (there is no fallback path).
 """
 from ._binding import (FLCE_BF16, FLCE_F32, FLCE_GRAD_MEAN, FLCE_GRAD_PER_TOKEN,  # noqa: F401
                        FLCE_GRAD_SUM, FlceError, FlceProblem, flce_backward, flce_forward,
-                       flce_last_error, flce_validate, flce_workspace_bytes, lib,
+                       flce_last_error, flce_set_timing_events, flce_validate,
+                       flce_workspace_bytes, lib,
                        linear_cross_entropy, make_problem)

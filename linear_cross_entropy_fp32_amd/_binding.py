@@ -22,7 +22,8 @@ ERROR_NAMES = {-1: "FLCE_ERR_NULL", -2: "FLCE_ERR_SHAPE", -3: "FLCE_ERR_DTYPE",
                -4: "FLCE_ERR_ALIGN", -5: "FLCE_ERR_WORKSPACE", -6: "FLCE_ERR_HIP",
                -7: "FLCE_ERR_ARG"}
 EXPORTED = ("flce_validate", "flce_workspace_bytes", "flce_forward", "flce_backward",
-            "flce_last_error", "flce_abi_version")
+            "flce_last_error", "flce_abi_version", "flce_set_timing_events")
+FLCE_KERNEL_FWD_STATS, FLCE_KERNEL_BWD_DZ, FLCE_KERNEL_CONTRACT = 0, 1, 2
 
 
 class FlceProblem(ctypes.Structure):
@@ -67,6 +68,8 @@ def lib() -> ctypes.CDLL:
         L.flce_last_error.restype = ctypes.c_char_p
         L.flce_abi_version.argtypes = []
         L.flce_abi_version.restype = ctypes.c_int
+        L.flce_set_timing_events.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_int]
+        L.flce_set_timing_events.restype = ctypes.c_int
         if L.flce_abi_version() != 1:
             raise RuntimeError("libflce.so ABI version mismatch: rebuild it")
         _lib = L
@@ -97,6 +100,15 @@ def flce_workspace_bytes(prob: FlceProblem) -> int:
 
 def flce_last_error() -> str:
     return lib().flce_last_error().decode()
+
+
+def flce_set_timing_events(kernel: int, events, n_pairs: int) -> int:
+    """Instrumentation: bracket `kernel`'s launches on this thread with the
+    given HIP events (a ctypes array of 2*n_pairs hipEvent_t); 0 clears."""
+    rc = lib().flce_set_timing_events(int(kernel), events, int(n_pairs))
+    if rc < 0:
+        raise FlceError(rc, flce_last_error())
+    return rc
 
 
 def _ptr(t: Optional[torch.Tensor]):

@@ -135,6 +135,30 @@ void logit_consts(const flce_problem* p, float& kx, float& c1, float& c2) {
   }
 }
 
+// Benchmark instrumentation: events recorded around one kernel's launches.
+struct LaunchTimer {
+  int kernel = -1;
+  hipEvent_t const* events = nullptr;
+  int n_pairs = 0, used = 0;
+};
+thread_local LaunchTimer g_timer;
+
+template <class F>
+hipError_t timed(int kernel, hipStream_t s, F&& launch) {
+  const bool on = g_timer.kernel == kernel && g_timer.used < g_timer.n_pairs;
+  if (on) {
+    const hipError_t e = hipEventRecord(g_timer.events[2 * g_timer.used], s);
+    if (e != hipSuccess) return e;
+  }
+  const hipError_t e = launch();
+  if (on && e == hipSuccess) {
+    const hipError_t e2 = hipEventRecord(g_timer.events[2 * g_timer.used + 1], s);
+    ++g_timer.used;
+    return e2;
+  }
+  return e;
+}
+
 int hip_check(hipError_t e, const char* what) {
   if (e != hipSuccess) return fail(FLCE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
   return FLCE_OK;
@@ -148,6 +172,19 @@ using namespace flce;
 extern "C" {
 
 int flce_abi_version(void) { return 1; }
+
+int flce_set_timing_events(int kernel, void* const* events, int n_pairs) {
+  g_err[0] = 0;
+  if (kernel < FLCE_KERNEL_FWD_STATS || kernel > FLCE_KERNEL_CONTRACT || n_pairs < 0 ||
+      (n_pairs > 0 && !events))
+    return fail(FLCE_ERR_ARG, "invalid timing-event request");
+  const int recorded = g_timer.used;
+  g_timer.kernel = n_pairs > 0 ? kernel : -1;
+  g_timer.events = reinterpret_cast<hipEvent_t const*>(events);
+  g_timer.n_pairs = n_pairs;
+  g_timer.used = 0;
+  return recorded;
+}
 
 const char* flce_last_error(void) { return g_err; }
 
@@ -223,7 +260,9 @@ int flce_forward(const flce_problem* p, const void* hidden, const void* weight,
     // softcapped logits lie below c: with 2c*log2(e) <= 120 the sums can use
     // the fixed reference c (no running max) without underflowing fp32
     const bool fixed_ref = p->softcap > 0 && 2.0 * p->softcap * 1.4426950408889634 <= 120.0;
-    if ((rc = hip_check(launch_fwd_stats(a, p->softcap > 0, fixed_ref, s), "fwd_stats")))
+    if ((rc = hip_check(timed(FLCE_KERNEL_FWD_STATS, s,
+                              [&] { return launch_fwd_stats(a, p->softcap > 0, fixed_ref, s); }),
+                        "fwd_stats")))
       return rc;
   }
   FinalArgs f{};
@@ -334,7 +373,10 @@ int flce_backward(const flce_problem* p, const void* hidden, const void* weight,
     const int64_t width = std::min<int64_t>(pl.vc, v - c0);
     d.c0 = (int)c0;
     d.chunk_tiles = (int)cdiv(width, kLogitTileV);
-    if ((rc = hip_check(launch_bwd_dz(d, p->softcap > 0, s), "bwd_dz"))) return rc;
+    if ((rc = hip_check(timed(FLCE_KERNEL_BWD_DZ, s,
+                              [&] { return launch_bwd_dz(d, p->softcap > 0, s); }),
+                        "bwd_dz")))
+      return rc;
 
     g.w = static_cast<const uint16_t*>(weight) + c0 * h;
     g.width = (int)width;
@@ -342,7 +384,9 @@ int flce_backward(const flce_problem* p, const void* hidden, const void* weight,
     g.gw = grad_weight + c0 * h;
     g.gw_m_tiles = (int)cdiv(width, kGemmTileM);
     g.gw_rows_per_unit = (int)cdiv(g.gw_m_tiles, pl.gh_splits);
-    if ((rc = hip_check(launch_contract(g, s), "contract"))) return rc;
+    if ((rc = hip_check(timed(FLCE_KERNEL_CONTRACT, s, [&] { return launch_contract(g, s); }),
+                        "contract")))
+      return rc;
 
     if (grad_bias &&
         (rc = hip_check(launch_colsum(dz, pl.vc, (int)n, (int)width, grad_bias + c0, s), "colsum")))

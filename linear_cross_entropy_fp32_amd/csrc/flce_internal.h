@@ -5,9 +5,12 @@
 
 namespace flce {
 
-// Logit tiles (forward stats, backward dz): 128 vocabulary rows x 256 tokens.
-constexpr int kLogitTileV = 128;
-constexpr int kLogitTileN = 256;
+// Logit tiles (forward stats, backward dz): vocabulary rows x tokens.
+#ifndef FLCE_LOGIT_TILE_V
+#define FLCE_LOGIT_TILE_V 128
+#endif
+constexpr int kLogitTileV = FLCE_LOGIT_TILE_V;
+constexpr int kLogitTileN = 32768 / FLCE_LOGIT_TILE_V;
 // Contraction tiles (grad_hidden, grad_weight): 256 x 128 outputs.
 constexpr int kGemmTileM = 256;
 constexpr int kGemmTileN = 128;

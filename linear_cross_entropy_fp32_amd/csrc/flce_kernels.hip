@@ -30,6 +30,8 @@ using LogitTile = Tile<kLogitTileV, kLogitTileN, kSliceK, true, true>;      // 1
 using GhTile = Tile<kGemmTileM, kGemmTileN, kSliceK, true, false>;          // dz . W
 using GwTile = Tile<kGemmTileM, kGemmTileN, kSliceK, false, false>;         // dz^T . h
 constexpr int kColumns = LogitTile::TN;      // token columns per lane
+constexpr int kQ = LogitTile::TM * 16;       // values per token column per lane
+constexpr int kWaveRows = kLogitTileV / 2;   // vocabulary rows per wave
 
 // ------------------------------------------------------------------ helpers
 
@@ -44,7 +46,7 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-// Row offset, inside a wave's 64 vocabulary rows, of value q (0..31) of a
+// Row offset, inside a wave's vocabulary rows, of value q (0..kQ-1) of a
 // lane's token column (q = 16 * block + accumulator register), not counting
 // the +4 of the lane's half-wave.
 __host__ __device__ constexpr int q_row(int q) {
@@ -106,22 +108,22 @@ __device__ __forceinline__ float final_u(float x, float kx, float bk, float c1, 
   }
 }
 
-// Bias terms (b * kx) of the 32 rows a lane holds in a wave's 64-row slab;
+// Bias terms (b * kx) of the kQ rows a lane holds in a wave's slab of rows;
 // rows past the vocabulary read zero through the buffer bound.
 template <bool BIAS>
 __device__ __forceinline__ void load_bias(const float* bias, int v, int vw, float kx,
-                                          float (&bk)[32]) {
+                                          float (&bk)[kQ]) {
   if constexpr (BIAS) {
     const int half = (threadIdx.x & 63) >> 5;
     const __amdgpu_buffer_rsrc_t rs = tile_rsrc(bias, (int64_t)v * 4);
 #pragma unroll
-    for (int q = 0; q < 32; ++q) {
+    for (int q = 0; q < kQ; ++q) {
       const uint32_t off = (uint32_t)(vw + q_row(q) + half * 4) * 4;
       bk[q] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0)) * kx;
     }
   } else {
 #pragma unroll
-    for (int q = 0; q < 32; ++q) bk[q] = 0.f;
+    for (int q = 0; q < kQ; ++q) bk[q] = 0.f;
   }
 }
 
@@ -147,7 +149,7 @@ __global__ void split_hidden_kernel(const float* __restrict__ h, uint16_t* __res
 }
 
 // ------------------------------------------------------------- forward: K1
-// Fold one token column (32 values in a lane) of a finished logit tile into
+// Fold one token column (kQ values in a lane) of a finished logit tile into
 // that token's state.  `val` holds the values in place of the accumulators.
 //
 // FIXED (softcap with 2c*log2e <= 120): every final logit is below c, so the
@@ -155,16 +157,16 @@ __global__ void split_hidden_kernel(const float* __restrict__ h, uint16_t* __res
 // value kept is d = u - c*log2e = -2c*log2e*r.  Otherwise the two-pass online
 // fold: tile max first, then the exponentials against the new reference.
 template <bool CAP, bool FIXED>
-__device__ __forceinline__ void fold_column(float (&val)[32], PartState& st, int tgt, int vw,
+__device__ __forceinline__ void fold_column(float (&val)[kQ], PartState& st, int tgt, int vw,
                                             int half) {
   float mt = val[0];
 #pragma unroll
-  for (int q = 1; q < 32; ++q) mt = fmaxf(mt, val[q]);
+  for (int q = 1; q < kQ; ++q) mt = fmaxf(mt, val[q]);
   // argmax: the first (lowest-row) position holding the tile maximum
   if (mt > st.bu) {
     int row = 0;
 #pragma unroll
-    for (int q = 31; q >= 0; --q)
+    for (int q = kQ - 1; q >= 0; --q)
       if (val[q] == mt) row = q_row(q);
     st.bu = mt;
     st.bi = vw + half * 4 + row;
@@ -172,16 +174,16 @@ __device__ __forceinline__ void fold_column(float (&val)[32], PartState& st, int
   // target value: only in lanes whose target row is one of their rows
   {
     const int rel = tgt - vw - half * 4;
-    if (rel >= 0 && rel < 64 && (rel & 4) == 0) {
+    if (rel >= 0 && rel < kWaveRows && (rel & 4) == 0) {
 #pragma unroll
-      for (int q = 0; q < 32; ++q)
+      for (int q = 0; q < kQ; ++q)
         if (q_row(q) == rel) st.zt = val[q];
     }
   }
   float s4[4] = {0.f, 0.f, 0.f, 0.f}, t4[4] = {0.f, 0.f, 0.f, 0.f};
   if constexpr (FIXED) {
 #pragma unroll
-    for (int q = 0; q < 32; ++q) {
+    for (int q = 0; q < kQ; ++q) {
       const float p = fast_exp2(val[q]);
       s4[q & 3] += p;
       t4[q & 3] = fmaf(p, val[q], t4[q & 3]);
@@ -194,7 +196,7 @@ __device__ __forceinline__ void fold_column(float (&val)[32], PartState& st, int
     if (mn > kMasked) {
       const float alpha = fast_exp2(st.m - mn);
 #pragma unroll
-      for (int q = 0; q < 32; ++q) {
+      for (int q = 0; q < kQ; ++q) {
         const float p = fast_exp2(val[q] - mn);
         s4[q & 3] += p;
         t4[q & 3] = fmaf(p, val[q], t4[q & 3]);
@@ -215,15 +217,15 @@ struct FwdEpilogue {
 
   __device__ __forceinline__ void operator()(int t, LogitTile& T) {
     const int v0 = (vt_begin + t) * kLogitTileV;
-    const int vw = v0 + wm * (kLogitTileV / 2);
+    const int vw = v0 + wm * kWaveRows;
     const bool tail = v0 + kLogitTileV > a.v;
-    float bk[32];
+    float bk[kQ];
     load_bias<BIAS>(a.bias, a.v, vw, a.kx, bk);
 #pragma unroll
     for (int j = 0; j < kColumns; ++j) {
-      float val[32];
+      float val[kQ];
 #pragma unroll
-      for (int q = 0; q < 32; ++q) {
+      for (int q = 0; q < kQ; ++q) {
         const float x = T.acc[q >> 4][j][q & 15];
         if constexpr (FIXED) {
           const float e = fast_exp2(fmaf(x, a.kx, bk[q]));
@@ -235,7 +237,7 @@ struct FwdEpilogue {
       }
       if (tail) {
 #pragma unroll
-        for (int q = 0; q < 32; ++q)
+        for (int q = 0; q < kQ; ++q)
           if (vw + half * 4 + q_row(q) >= a.v) val[q] = kMasked;
       }
       fold_column<CAP, FIXED>(val, st[j], tgt[j], vw, half);
@@ -422,15 +424,15 @@ struct DzEpilogue {
 
   __device__ __forceinline__ void operator()(int t, LogitTile& T) {
     const int v0 = a.c0 + (vt_begin + t) * kLogitTileV;
-    const int vw = v0 + wm * (kLogitTileV / 2);
+    const int vw = v0 + wm * kWaveRows;
     const bool tail = v0 + kLogitTileV > a.v;
-    float bk[32];
+    float bk[kQ];
     load_bias<BIAS>(a.bias, a.v, vw, a.kx, bk);
 #pragma unroll
     for (int j = 0; j < kColumns; ++j) {
-      float d[32];
+      float d[kQ];
 #pragma unroll
-      for (int q = 0; q < 32; ++q) {
+      for (int q = 0; q < kQ; ++q) {
         const float x = T.acc[q >> 4][j][q & 15];
         if constexpr (CAP) {
           const float e = fast_exp2(fmaf(x, a.kx, bk[q]));
@@ -444,9 +446,9 @@ struct DzEpilogue {
       // one-hot term, only in lanes whose target row is one of their rows
       {
         const int rel = tgt[j] - vw - half * 4;
-        if (rel >= 0 && rel < 64 && (rel & 4) == 0) {
+        if (rel >= 0 && rel < kWaveRows && (rel & 4) == 0) {
 #pragma unroll
-          for (int q = 0; q < 32; ++q)
+          for (int q = 0; q < kQ; ++q)
             if (q_row(q) == rel) {
               if constexpr (CAP) {
                 const float e = fast_exp2(fmaf(T.acc[q >> 4][j][q & 15], a.kx, bk[q]));
@@ -460,13 +462,13 @@ struct DzEpilogue {
       }
       if (tail) {
 #pragma unroll
-        for (int q = 0; q < 32; ++q)
+        for (int q = 0; q < kQ; ++q)
           if (vw + half * 4 + q_row(q) >= a.v) d[q] = 0.f;
       }
       if (nrow[j] >= 0) {
         uint16_t* row = a.dz + (int64_t)nrow[j] * a.ldz + (vw - a.c0) + half * 4;
 #pragma unroll
-        for (int g4 = 0; g4 < 8; ++g4) {
+        for (int g4 = 0; g4 < kQ / 4; ++g4) {
           u32x2 pk;
           pk[0] = pack_bf16x2(d[g4 * 4 + 0], d[g4 * 4 + 1]);
           pk[1] = pack_bf16x2(d[g4 * 4 + 2], d[g4 * 4 + 3]);

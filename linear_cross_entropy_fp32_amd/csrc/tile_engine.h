@@ -75,9 +75,11 @@ template <int BK>
 struct LdsLayout {
   static constexpr int kChunks = BK / 8;       // 16-byte chunks per row
   static constexpr int kRowBytes = BK * 2;
+  // Chunk swizzle chosen by measurement (SQ_LDS_BANK_CONFLICT): with 64-byte
+  // rows the rows r and r+4 share banks, so the chunk is XORed with r/4.
   __device__ static __forceinline__ int swz(int r) {
     if constexpr (BK == 64) return (r ^ (r >> 3)) & 7;
-    else return ((r >> 1) ^ (r >> 3)) & 3;
+    else return (r >> 2) & 3;
   }
   __device__ static __forceinline__ int off(int r, int c) {
     return r * kRowBytes + ((c ^ swz(r)) << 4);
