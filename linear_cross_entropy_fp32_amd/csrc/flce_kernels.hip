@@ -26,9 +26,12 @@ constexpr float kNegInf = -__builtin_huge_valf();
 // every real logit, and 2^(it - m) is exactly 0 with 0 * it finite.
 constexpr float kMasked = -3.0e38f;
 
-using LogitTile = Tile<kLogitTileV, kLogitTileN, kSliceK, true, true>;      // 128 x 256
-using GhTile = Tile<kGemmTileM, kGemmTileN, kSliceK, true, false>;          // dz . W
-using GwTile = Tile<kGemmTileM, kGemmTileN, kSliceK, false, false>;         // dz^T . h
+static_assert(kSliceK == kBK, "slice depth");
+static_assert(4 * 32 * (kLogitTileV / 2) * 2 <= Tile<kLogitTileV, kLogitTileN, true, true>::kStage,
+              "dz transpose buffer fits one LDS stage");
+using LogitTile = Tile<kLogitTileV, kLogitTileN, true, true>;      // 128 x 256
+using GhTile = Tile<kGemmTileM, kGemmTileN, true, false>;          // dz . W
+using GwTile = Tile<kGemmTileM, kGemmTileN, false, false>;         // dz^T . h
 constexpr int kColumns = LogitTile::TN;      // token columns per lane
 constexpr int kQ = LogitTile::TM * 16;       // values per token column per lane
 constexpr int kWaveRows = kLogitTileV / 2;   // vocabulary rows per wave
@@ -210,12 +213,13 @@ __device__ __forceinline__ void fold_column(float (&val)[kQ], PartState& st, int
 
 template <bool CAP, bool FIXED, bool BIAS>
 struct FwdEpilogue {
+  static constexpr bool kUsesLds = false;
   const FwdArgs& a;
   PartState (&st)[kColumns];
   const int (&tgt)[kColumns];
   int vt_begin, wm, half;
 
-  __device__ __forceinline__ void operator()(int t, LogitTile& T) {
+  __device__ __forceinline__ void operator()(int t, LogitTile& T, char*) {
     const int v0 = (vt_begin + t) * kLogitTileV;
     const int vw = v0 + wm * kWaveRows;
     const bool tail = v0 + kLogitTileV > a.v;
@@ -415,19 +419,32 @@ __device__ __forceinline__ float row_grad(const DzArgs& a, int n, int64_t t) {
 
 template <bool CAP, bool BIAS>
 struct DzEpilogue {
+  // The finished tile is transposed through a free LDS stage so that every
+  // store covers whole 128-byte rows of dz (8 lanes per token).
+  static constexpr bool kUsesLds = true;
   const DzArgs& a;
   const float (&gs)[kColumns];     // g_n * s (times 4 with softcap: the slope is 4 r (1-r))
   const float (&nl)[kColumns];     // -lse_n in base-2 units
   const int (&tgt)[kColumns];
-  const int (&nrow)[kColumns];
-  int vt_begin, wm, half;
+  int vt_begin, wm, half, nbase;   // nbase: first token of the wave's columns
 
-  __device__ __forceinline__ void operator()(int t, LogitTile& T) {
+  __device__ __forceinline__ void operator()(int t, LogitTile& T, char* free_lds) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int v0 = a.c0 + (vt_begin + t) * kLogitTileV;
-    const int vw = v0 + wm * kWaveRows;
+    const int vw = __builtin_amdgcn_readfirstlane(v0 + wm * kWaveRows);
     const bool tail = v0 + kLogitTileV > a.v;
     float bk[kQ];
     load_bias<BIAS>(a.bias, a.v, vw, a.kx, bk);
+    // [32 tokens][64 vocabulary rows] bf16 of this wave; the 8-byte piece p of
+    // token row tl is stored at piece p ^ (tl / 2), which keeps both the
+    // 8-byte writes and the 16-byte reads below free of bank conflicts
+    char* buf = free_lds + wave * (32 * kWaveRows * 2);
+    // stores: base at row nbase of the chunk, bounded by the end of row N-1,
+    // so stores of rows >= N are dropped
+    const uint32_t ld_bytes = (uint32_t)a.ldz * 2;
+    const __amdgpu_buffer_rsrc_t out =
+        tile_rsrc(a.dz + (int64_t)nbase * a.ldz, (int64_t)(a.n - nbase) * ld_bytes);
+    const uint32_t voff = (uint32_t)(lane >> 3) * ld_bytes + (lane & 7) * 16 + (vw - a.c0) * 2;
 #pragma unroll
     for (int j = 0; j < kColumns; ++j) {
       float d[kQ];
@@ -465,15 +482,27 @@ struct DzEpilogue {
         for (int q = 0; q < kQ; ++q)
           if (vw + half * 4 + q_row(q) >= a.v) d[q] = 0.f;
       }
-      if (nrow[j] >= 0) {
-        uint16_t* row = a.dz + (int64_t)nrow[j] * a.ldz + (vw - a.c0) + half * 4;
+      {
+        const int tl = lane & 31;
+        char* trow = buf + tl * (kWaveRows * 2);
 #pragma unroll
         for (int g4 = 0; g4 < kQ / 4; ++g4) {
           u32x2 pk;
           pk[0] = pack_bf16x2(d[g4 * 4 + 0], d[g4 * 4 + 1]);
           pk[1] = pack_bf16x2(d[g4 * 4 + 2], d[g4 * 4 + 3]);
-          *reinterpret_cast<u32x2*>(row + q_row(g4 * 4)) = pk;
+          const int piece = q_row(g4 * 4) / 4 + half;
+          *reinterpret_cast<u32x2*>(trow + ((piece ^ (tl >> 1)) << 3)) = pk;
         }
+      }
+#pragma unroll
+      for (int pass = 0; pass < 4; ++pass) {
+        const int tr = pass * 8 + (lane >> 3), c = lane & 7, f = tr >> 1;
+        u32x4 x = *reinterpret_cast<const u32x4*>(buf + tr * (kWaveRows * 2) + ((c ^ (f >> 1)) << 4));
+        if (f & 1) x = __builtin_shufflevector(x, x, 2, 3, 0, 1);
+        // token nbase + j*32 + tr; tokens past N fall outside the descriptor
+        // (the whole offset goes in the lane offset: the scalar offset is not
+        // part of the range check)
+        __builtin_amdgcn_raw_buffer_store_b128(x, out, voff + (j * 32 + pass * 8) * ld_bytes, 0, 0);
       }
     }
   }
@@ -491,7 +520,7 @@ bwd_dz_kernel(const DzArgs a) {
   const int half = lane >> 5;
 
   float gs[kColumns], nl[kColumns];
-  int tgt[kColumns], nrow[kColumns];
+  int tgt[kColumns];
 #pragma unroll
   for (int j = 0; j < kColumns; ++j) {
     const int n = n0 + wn * (kLogitTileN / 2) + j * 32 + (lane & 31);
@@ -499,14 +528,14 @@ bwd_dz_kernel(const DzArgs a) {
     gs[j] = row_grad(a, n, t) * (CAP ? 4.0f : 1.0f);
     nl[j] = (n < a.n) ? -a.lse[n] * kLog2e : 0.f;
     tgt[j] = (t >= 0 && t < a.v) ? (int)t : -(1 << 30);
-    nrow[j] = (n < a.n) ? n : -1;
   }
   const int vt_begin = grp * a.tiles_per_wg;
   const int ntiles = min(a.chunk_tiles, vt_begin + a.tiles_per_wg) - vt_begin;
   const Operand opA{a.w, a.hdim, a.c0 + vt_begin * kLogitTileV, a.v, a.hdim};
   const Operand opB0{a.h0, a.hdim, n0, a.n, a.hdim};
   const Operand opB1{a.h1 ? a.h1 : a.h0, a.hdim, n0, a.n, a.hdim};
-  DzEpilogue<CAP, BIAS> epi{a, gs, nl, tgt, nrow, vt_begin, wm, half};
+  DzEpilogue<CAP, BIAS> epi{a, gs, nl, tgt, vt_begin, wm, half,
+                           __builtin_amdgcn_readfirstlane(n0 + wn * (kLogitTileN / 2))};
   LogitTile T;
   T.run_stream(lds, opA, opB0, opB1, a.h1 != nullptr, a.hdim, ntiles, epi);
 }

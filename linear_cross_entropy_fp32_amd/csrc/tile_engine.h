@@ -5,23 +5,34 @@
 // (v_mfma_f32_32x32x16_bf16); each wave owns TM x TN blocks of 32 x 32
 // (TM = BM/64, TN = BN/64).
 //
-// Operands move HBM -> registers -> LDS in K slices of BK (32 or 64) values.
-// Two register sets hold the next two slices while the current one is
-// multiplied out of LDS, so a slice's global loads have two slices of MFMA
-// work to land; LDS is double buffered.  In LDS each operand row (one M or N
-// index) holds BK consecutive K values as 16-byte chunks whose positions are
-// XOR-swizzled by the row, so that the MFMA fragment reads (eight consecutive
-// rows, one chunk) and the staging stores are bank-conflict free.
+// Operands stream HBM -> LDS in K slices of 32 values through a ring of three
+// LDS stages that buffer loads write directly (buffer_load_dwordx4 ... lds,
+// "LDS DMA"): no staging registers and no LDS store instructions.  Slice kt+2 is issued while
+// slice kt is multiplied, and slice kt is consumed after an explicit
+// "s_waitcnt vmcnt(loads of one slice)" + s_barrier, so only that slice has to
+// have landed (a fenced barrier would make the compiler drain every
+// outstanding load).  Loads return in order, so the wait also holds when the
+// caller's epilogue has issued other memory operations in between.
+// Out-of-range rows and K values read zero through the buffer descriptor
+// bound; no load is branched around.
 //
-// An operand whose K index is contiguous in memory is copied 16 bytes at a
-// time and read back with one ds_read_b128 per MFMA fragment.  An operand whose
-// M/N index is contiguous (the lm_head read along the vocabulary, the hidden
-// states read along tokens) is stored in LDS as it lies in memory, one padded
-// row per K index, and each fragment is read with two ds_read_b64_tr_b16:
-// within every 16-lane group, lane j receives element j%4 of the 64-bit piece
-// addressed by lane 4e + j/4 as its element e, so lane 16g+i addresses K row
-// k0 + 8(g/2) + i/4 (+4 for the second read) at column m0 + 16(g%2) + 4(i%4)
-// and ends up holding the 8 consecutive K values of column m0 + (lane % 32).
+// LDS layouts.  One LDS-DMA instruction writes 64 lanes x 16 bytes to 1 KB of
+// consecutive LDS; each lane picks the global 16-byte chunk that belongs in
+// its slot, which is how the layouts below are swizzled.
+//  * K-major operand (K contiguous in memory: lm_head rows, hidden rows, dz
+//    rows): one 64-byte row per M/N index; chunk c of row r sits at position
+//    c ^ ((r / 4) % 4), which makes the fragment reads (8 consecutive K values
+//    per lane, one ds_read_b128) free of bank conflicts.
+//  * MN-major operand (M/N contiguous: lm_head read along the vocabulary,
+//    hidden read along tokens, dz read along the vocabulary): one row per K
+//    index holding the tile's M/N values; chunk c of K row k sits at position
+//    c ^ (4 (k % 4)).  A fragment is two ds_read_b64_tr_b16: within every
+//    16-lane group, lane j receives element j%4 of the 64-bit piece addressed
+//    by lane 4e + j/4 as its element e, so lane 16g+i addresses K row
+//    k0 + 8(g/2) + i/4 (+4 for the second read) at column m0 + 16(g%2) +
+//    4(i%4), and holds the 8 consecutive K values of column m0 + lane%32.
+//    The 32 lanes served in one LDS cycle then touch 8 distinct 32-byte
+//    pieces of the 256-byte bank window.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -32,8 +43,12 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kThreads = 256;
+constexpr int kBK = 32;        // K values per slice
+constexpr int kStages = 3;     // LDS ring depth
 
 // Row (within a 32x32 block) of accumulator register r of lane l for the
 // 32x32x16 MFMA; the column is l % 32.
@@ -42,8 +57,8 @@ __device__ __forceinline__ int acc_row(int r, int lane) {
 }
 
 // Operand descriptor.  K-major: element (row, k) at ptr[row * ld + k]; the row
-// bound is exact and K is checked per 8-value chunk (callers keep K % 8 == 0
-// or zero padding).  MN-major: element (row, k) at ptr[k * ld + row]; rows are
+// bound is exact, K is checked per 8-value chunk (callers keep K % 8 == 0 or
+// zero padding).  MN-major: element (row, k) at ptr[k * ld + row]; rows are
 // checked per group of 8 (callers keep the bound a multiple of 8), K exactly.
 struct Operand {
   const uint16_t* ptr;
@@ -52,15 +67,6 @@ struct Operand {
   int row_bound;
   int k_bound;
 };
-
-// Workgroup barrier that orders LDS only.  __syncthreads() also fences global
-// memory, which makes the compiler drain every outstanding global load (the
-// prefetched slices) at each barrier.
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
 
 constexpr uint32_t kOutOfRange = 0x80000000u;   // buffer offset that reads as zero
 
@@ -71,134 +77,176 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void* base, in
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)b, 0x00020000);
 }
 
-template <int BK>
-struct LdsLayout {
-  static constexpr int kChunks = BK / 8;       // 16-byte chunks per row
-  static constexpr int kRowBytes = BK * 2;
-  // Chunk swizzle chosen by measurement (SQ_LDS_BANK_CONFLICT): with 64-byte
-  // rows the rows r and r+4 share banks, so the chunk is XORed with r/4.
-  __device__ static __forceinline__ int swz(int r) {
-    if constexpr (BK == 64) return (r ^ (r >> 3)) & 7;
-    else return (r >> 2) & 3;
-  }
-  __device__ static __forceinline__ int off(int r, int c) {
-    return r * kRowBytes + ((c ^ swz(r)) << 4);
-  }
-};
+// `off` when `in_range`, else an offset that reads zero.  Written as bit
+// arithmetic (kept opaque) so that the compiler does not split the load that
+// uses it into two predicated copies.
+__device__ __forceinline__ uint32_t offset_or_oob(bool in_range, uint32_t off) {
+  uint32_t m = in_range ? 0u : kOutOfRange;
+  asm("" : "+v"(m));
+  return off | m;
+}
 
-template <int R, int BK, bool KMAJ>
+// Buffer descriptor as four scalar registers (base, stride 0, size in bytes,
+// the data format word of a raw buffer) for the LDS-DMA loads below.
+__device__ __forceinline__ u32x4 dma_rsrc(const void* base, int64_t bytes) {
+  const int64_t b = bytes < 0 ? 0 : (bytes > 0x7fffffffLL ? 0x7fffffffLL : bytes);
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  u32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  r[1] = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32) & 0xffffu);
+  r[2] = __builtin_amdgcn_readfirstlane((uint32_t)b);
+  r[3] = 0x00020000u;
+  return r;
+}
+
+// 16 bytes per lane from global memory into LDS: lane l of the wave writes
+// bytes [16 l, 16 l + 16) of the 1 KB block at `lds` (wave-uniform); offsets
+// at or past the descriptor size read zero.  Issued as inline assembly so that
+// the compiler does not track the LDS writes: it would otherwise wait for
+// every outstanding load before each transposing LDS read.  Completion is
+// ordered by vm_barrier() alone; the waits the compiler places for its own
+// loads stay sufficient, since loads return in order and these only add to
+// the count.  Being volatile, the statement keeps its place between the
+// barriers.  The s_nop covers the one wait state that GFX9 needs between an
+// M0 write and an LDS-DMA instruction.
+__device__ __forceinline__ void dma16(const u32x4& rs, const char* lds, uint32_t off) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)lds);
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(off), "s"(rs),
+               "{m0}"(m0));
+}
+
+// Wait until at most N of this wave's vector memory operations are
+// outstanding, then barrier the workgroup.
+template <int N>
+__device__ __forceinline__ void vm_barrier() {
+  static_assert(N >= 0 && N <= 12, "vmcnt immediate");
+  // lgkmcnt(0): this wave's LDS reads of the stage about to be refilled are done
+  if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  else if constexpr (N == 1) asm volatile("s_waitcnt vmcnt(1) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  else if constexpr (N == 2) asm volatile("s_waitcnt vmcnt(2) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  else if constexpr (N == 3) asm volatile("s_waitcnt vmcnt(3) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  else if constexpr (N == 4) asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  else if constexpr (N == 5) asm volatile("s_waitcnt vmcnt(5) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  else if constexpr (N == 6) asm volatile("s_waitcnt vmcnt(6) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  else if constexpr (N == 7) asm volatile("s_waitcnt vmcnt(7) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  else if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  else if constexpr (N == 9) asm volatile("s_waitcnt vmcnt(9) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  else if constexpr (N == 10) asm volatile("s_waitcnt vmcnt(10) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  else if constexpr (N == 11) asm volatile("s_waitcnt vmcnt(11) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(12) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Workgroup barrier after this wave's LDS accesses have completed; loads
+// into LDS that are still in flight stay in flight.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// --------------------------------------------------------------- operands
+
+template <int R, bool KMAJ>
 struct Stage;
 
-template <int R, int BK>
-struct Stage<R, BK, true> {
-  using L = LdsLayout<BK>;
-  static constexpr int kN = R * L::kChunks / kThreads;
-  static_assert(kN >= 1, "tile too small for the K-major loader");
-  u32x4 reg[kN];
+template <int R>
+struct Stage<R, true> {
+  static constexpr int kRowBytes = kBK * 2;                 // 64
+  static constexpr int kBytes = R * kRowBytes;
+  static constexpr int kPerWave = R * (kBK / 8) / 4 / 64;   // DMA instructions per wave
+  static_assert(kPerWave >= 1 && R % 64 == 0, "K-major tile shape");
+  __device__ static __forceinline__ int swz(int r) { return (r >> 2) & 3; }
 
-  // rows of the tile beyond the operand's row bound fall outside the
-  // descriptor; chunks beyond the K bound are sent out of range explicitly.
   struct Src {
-    __amdgpu_buffer_rsrc_t rsrc;
+    u32x4 rsrc;
     uint32_t ld_bytes;
     int k_bound;
   };
+  // rows past the operand's row bound fall outside the descriptor; chunks
+  // past the K bound are sent out of range explicitly
   __device__ static __forceinline__ Src source(const Operand& op) {
     const int64_t rows = (int64_t)op.row_bound - op.row0;
-    return Src{tile_rsrc(op.ptr + (int64_t)op.row0 * op.ld, rows * op.ld * 2),
+    return Src{dma_rsrc(op.ptr + (int64_t)op.row0 * op.ld, rows * op.ld * 2),
                (uint32_t)(op.ld * 2), op.k_bound};
   }
-  __device__ __forceinline__ void load(const Src& s, int k0) {
+  __device__ static __forceinline__ void issue(const Src& s, char* lds, int k0) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
-    for (int i = 0; i < kN; ++i) {
-      const int q = threadIdx.x + i * kThreads;
-      const int row = q / L::kChunks, c = q % L::kChunks;
+    for (int i = 0; i < kPerWave; ++i) {
+      const int blk = wave * kPerWave + i;          // 1 KB block = 16 rows
+      const int p = blk * 64 + lane;                // 16-byte slot this lane writes
+      const int row = p >> 2, c = (p & 3) ^ swz(row);
       const int gk = k0 + c * 8;
-      const uint32_t off = gk < s.k_bound ? row * s.ld_bytes + gk * 2 : kOutOfRange;
-      reg[i] = __builtin_amdgcn_raw_buffer_load_b128(s.rsrc, off, 0, 0);
+      dma16(s.rsrc, lds + blk * 1024, offset_or_oob(gk < s.k_bound, row * s.ld_bytes + gk * 2));
     }
   }
-  __device__ __forceinline__ void store(char* lds) const {
-#pragma unroll
-    for (int i = 0; i < kN; ++i) {
-      const int q = threadIdx.x + i * kThreads;
-      *reinterpret_cast<u32x4*>(lds + L::off(q / L::kChunks, q % L::kChunks)) = reg[i];
-    }
+  // 8 consecutive K values (from 16 ks + 8 (lane / 32)) of row m0 + lane % 32
+  __device__ static __forceinline__ bf16x8 frag(const char* lds, int m0, int ks) {
+    const int lane = threadIdx.x & 63;
+    const int r = m0 + (lane & 31), c = ks * 2 + (lane >> 5);
+    return *reinterpret_cast<const bf16x8*>(lds + r * kRowBytes + ((c ^ swz(r)) << 4));
   }
 };
 
-template <int R, int BK>
-struct Stage<R, BK, false> {
-  static constexpr int kRowBytes = R * 2 + 32;        // padded: 4 K rows hit distinct banks
-  static constexpr int kBytes = BK * kRowBytes;
-  static constexpr int kCPR = R / 8;                  // 16-byte chunks per K row
-  static constexpr int kN = BK * kCPR / kThreads;
-  static_assert(kN >= 1 && (BK * kCPR) % kThreads == 0, "MN-major tile shape");
-  u32x4 reg[kN];
+template <int R>
+struct Stage<R, false> {
+  static constexpr int kRowBytes = R * 2;                   // one K row
+  static constexpr int kBytes = kBK * kRowBytes;
+  static constexpr int kCPR = R / 8;                        // chunks per K row
+  static constexpr int kPerWave = kBK * kCPR / 4 / 64;
+  static_assert(kPerWave >= 1 && kCPR >= 16 && kCPR % 16 == 0, "MN-major tile shape");
+  __device__ static __forceinline__ int swz(int k) { return (k & 3) << 2; }
 
-  // k beyond the K bound falls outside the descriptor; chunks beyond the row
-  // bound are sent out of range explicitly.
   struct Src {
-    __amdgpu_buffer_rsrc_t rsrc;
+    u32x4 rsrc;
     uint32_t ld_bytes;
     int rows;       // valid rows from row0
   };
+  // K rows past the K bound fall outside the descriptor; chunks past the row
+  // bound are sent out of range explicitly
   __device__ static __forceinline__ Src source(const Operand& op) {
-    return Src{tile_rsrc(op.ptr + op.row0, ((int64_t)op.k_bound * op.ld - op.row0) * 2),
+    return Src{dma_rsrc(op.ptr + op.row0, ((int64_t)op.k_bound * op.ld - op.row0) * 2),
                (uint32_t)(op.ld * 2), op.row_bound - op.row0};
   }
-  __device__ __forceinline__ void load(const Src& s, int k0) {
+  __device__ static __forceinline__ void issue(const Src& s, char* lds, int k0) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
-    for (int i = 0; i < kN; ++i) {
-      const int q = threadIdx.x + i * kThreads;
-      const int k = q / kCPR, c = q % kCPR;
-      const uint32_t off = c * 8 < s.rows ? (uint32_t)(k0 + k) * s.ld_bytes + c * 16 : kOutOfRange;
-      reg[i] = __builtin_amdgcn_raw_buffer_load_b128(s.rsrc, off, 0, 0);
+    for (int i = 0; i < kPerWave; ++i) {
+      const int blk = wave * kPerWave + i;
+      const int p = blk * 64 + lane;
+      const int k = p / kCPR, c = (p % kCPR) ^ swz(k);
+      dma16(s.rsrc, lds + blk * 1024,
+            offset_or_oob(c * 8 < s.rows, (uint32_t)(k0 + k) * s.ld_bytes + c * 16));
     }
   }
-  __device__ __forceinline__ void store(char* lds) const {
-#pragma unroll
-    for (int i = 0; i < kN; ++i) {
-      const int q = threadIdx.x + i * kThreads;
-      *reinterpret_cast<u32x4*>(lds + (q / kCPR) * kRowBytes + (q % kCPR) * 16) = reg[i];
-    }
-  }
-};
-
-// MFMA fragment (8 consecutive K values of row m0 + lane % 32, starting at K
-// offset 16 ks + 8 (lane / 32)) from an LDS operand tile.
-template <int R, int BK, bool KMAJ>
-__device__ __forceinline__ bf16x8 read_frag(const char* lds, int m0, int ks) {
-  const int lane = threadIdx.x & 63;
-  if constexpr (KMAJ) {
-    return *reinterpret_cast<const bf16x8*>(
-        lds + LdsLayout<BK>::off(m0 + (lane & 31), ks * 2 + (lane >> 5)));
-  } else {
-    typedef short i16x4 __attribute__((ext_vector_type(4)));
-    constexpr int kRowBytes = Stage<R, BK, false>::kRowBytes;
+  // 8 consecutive K values (from 16 ks + 8 (lane / 32)) of column m0 + lane % 32
+  __device__ static __forceinline__ bf16x8 frag(const char* lds, int m0, int ks) {
+    const int lane = threadIdx.x & 63;
     const int g = lane >> 4, i = lane & 15;
-    const int k = ks * 16 + ((g >> 1) << 3) + (i >> 2);
+    const int k = ks * 16 + ((g >> 1) << 3) + (i >> 2);     // k % 4 == (k + 4) % 4
     const int m = m0 + ((g & 1) << 4) + ((i & 3) << 2);
-    const char* p = lds + k * kRowBytes + m * 2;
+    const int pos = ((((m >> 3) ^ swz(k)) << 4) | ((m & 7) << 1));
+    const char* p0 = lds + k * kRowBytes + pos;
     const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) i16x4*)(p));
+        (__attribute__((address_space(3))) i16x4*)(p0));
     const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) i16x4*)(p + 4 * kRowBytes));
-    typedef short i16x8 __attribute__((ext_vector_type(8)));
+        (__attribute__((address_space(3))) i16x4*)(p0 + 4 * kRowBytes));
     const i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
     return __builtin_bit_cast(bf16x8, v);
   }
-}
+};
 
-template <int BM, int BN, int BK, bool A_KMAJ, bool B_KMAJ>
+// ------------------------------------------------------------------- tile
+
+template <int BM, int BN, bool A_KMAJ, bool B_KMAJ>
 struct Tile {
   static constexpr int kBM = BM, kBN = BN;
   static constexpr int TM = BM / 64, TN = BN / 64;
-  using L = LdsLayout<BK>;
-  static constexpr int kLdsA = A_KMAJ ? BM * L::kRowBytes : Stage<BM, BK, false>::kBytes;
-  static constexpr int kLdsB = B_KMAJ ? BN * L::kRowBytes : Stage<BN, BK, false>::kBytes;
-  static constexpr int kStage = kLdsA + kLdsB;
-  static constexpr int kLdsBytes = 2 * kStage;
+  using SA = Stage<BM, A_KMAJ>;
+  using SB = Stage<BN, B_KMAJ>;
+  static constexpr int kLdsA = SA::kBytes;
+  static constexpr int kStage = SA::kBytes + SB::kBytes;
+  static constexpr int kLdsBytes = kStages * kStage;
+  static constexpr int kLoads = SA::kPerWave + SB::kPerWave;   // per wave per slice
 
   f32x16 acc[TM][TN];
 
@@ -214,15 +262,13 @@ struct Tile {
   __device__ __forceinline__ void mma_stage(const char* lds) {
     const int wave = threadIdx.x >> 6;
     const int wm = wave & 1, wn = wave >> 1;
-    const char* la = lds;
-    const char* lb = lds + kLdsA;
 #pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
+    for (int ks = 0; ks < kBK / 16; ++ks) {
       bf16x8 fa[TM], fb[TN];
 #pragma unroll
-      for (int j = 0; j < TN; ++j) fb[j] = read_frag<BN, BK, B_KMAJ>(lb, wn * (BN / 2) + j * 32, ks);
+      for (int j = 0; j < TN; ++j) fb[j] = SB::frag(lds + kLdsA, wn * (BN / 2) + j * 32, ks);
 #pragma unroll
-      for (int i = 0; i < TM; ++i) fa[i] = read_frag<BM, BK, A_KMAJ>(la, wm * (BM / 2) + i * 32, ks);
+      for (int i = 0; i < TM; ++i) fa[i] = SA::frag(lds, wm * (BM / 2) + i * 32, ks);
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -231,135 +277,99 @@ struct Tile {
     }
   }
 
-  using SA = Stage<BM, BK, A_KMAJ>;
-  using SB = Stage<BN, BK, B_KMAJ>;
-
-  __device__ static __forceinline__ void issue(SA& sa, SB& sb, const typename SA::Src& a,
+  // Slice `kt` of a one- or two-segment K range [k_begin, k_begin + 32 kt_seg)
+  // into LDS stage `buf`.  Segment 1 (the low half of a split fp32 operand)
+  // reuses A and takes B from b1.  Slices past the end read zero.
+  __device__ __forceinline__ static void issue(char* buf, const typename SA::Src& a,
                                                const typename SB::Src& b0,
                                                const typename SB::Src& b1, int kt_seg,
                                                int k_begin, int kt) {
     const int seg = kt >= kt_seg ? 1 : 0;
-    const int k0 = k_begin + (kt - seg * kt_seg) * BK;
-    sa.load(a, k0);
-    if (seg) {
-      sb.load(b1, k0);
-    } else {
-      sb.load(b0, k0);
-    }
+    const int k0 = k_begin + (kt - seg * kt_seg) * kBK;
+    SA::issue(a, buf, k0);
+    SB::issue(seg ? b1 : b0, buf + kLdsA, k0);
   }
 
-  // Accumulate over k in [k_begin, k_end) for one K segment, or two when
-  // two_seg is set: the second reuses A and takes B from b1 (the low half of
-  // a split fp32 operand).
+  // Accumulate over k in [k_begin, k_end), or twice over it when two_seg is
+  // set (A against b0, then against b1).  The range is read in whole slices:
+  // k_end - k_begin must be a multiple of 32 unless k_end is the operands' K
+  // bound (past which loads read zero).
   __device__ __forceinline__ void run(char* lds, const Operand a_op, const Operand b0_op,
                                       const Operand b1_op, bool two_seg, int k_begin, int k_end) {
-    const int kt_seg = (k_end - k_begin + BK - 1) / BK;
+    const int kt_seg = (k_end - k_begin + kBK - 1) / kBK;
     if (kt_seg <= 0) return;
     const int kt_total = kt_seg * (two_seg ? 2 : 1);
     const typename SA::Src a = SA::source(a_op);
     const typename SB::Src b0 = SB::source(b0_op);
     const typename SB::Src b1 = SB::source(two_seg ? b1_op : b0_op);
-    SA sa0, sa1;
-    SB sb0, sb1;
-    issue(sa0, sb0, a, b0, b1, kt_seg, k_begin, 0);
-    issue(sa1, sb1, a, b0, b1, kt_seg, k_begin, 1);
-    sa0.store(lds);
-    sb0.store(lds + kLdsA);
-    lds_barrier();
-    int kt = 0;
-    // Unrolled by two so each register set keeps a fixed name.
-    for (; kt + 1 < kt_total; kt += 2) {
-      // even step: compute buffer 0; set 0 is free, set 1 holds slice kt+1
-      // past the last slice the loads fall out of range and read zeros; issuing
-      // them unconditionally keeps the outstanding-load count static
-      issue(sa0, sb0, a, b0, b1, kt_seg, k_begin, kt + 2);
-      __builtin_amdgcn_sched_barrier(0);
-      mma_stage(lds);
-      sa1.store(lds + kStage);
-      sb1.store(lds + kStage + kLdsA);
-      lds_barrier();
-      // odd step: compute buffer 1; set 1 is free, set 0 holds slice kt+2
-      issue(sa1, sb1, a, b0, b1, kt_seg, k_begin, kt + 3);
-      __builtin_amdgcn_sched_barrier(0);
-      mma_stage(lds + kStage);
-      if (kt + 2 < kt_total) {
-        sa0.store(lds);
-        sb0.store(lds + kLdsA);
-      }
-      lds_barrier();
+    const int past = 2 * kt_seg;       // a slice index that reads zero in both modes
+    issue(lds, a, b0, b1, kt_seg, k_begin, 0);
+    issue(lds + kStage, a, b0, b1, kt_seg, k_begin, kt_total > 1 ? 1 : past);
+    int slot = 0, nslot = 2;
+    for (int kt = 0; kt < kt_total; ++kt) {
+      vm_barrier<kLoads>();            // slice kt landed; slice kt-1 no longer read
+      issue(lds + nslot * kStage, a, b0, b1, kt_seg, k_begin, kt + 2 < kt_total ? kt + 2 : past);
+      mma_stage(lds + slot * kStage);
+      slot = slot == kStages - 1 ? 0 : slot + 1;
+      nslot = nslot == kStages - 1 ? 0 : nslot + 1;
     }
-    if (kt < kt_total) {   // odd number of slices: the last one sits in buffer 0
-      mma_stage(lds);
-      lds_barrier();
-    }
+    vm_barrier<0>();
   }
 
   // Streams `ntiles` tiles that share the B operand and take A rows
-  // a.row0 + t * BM (t = 0 .. ntiles-1), keeping the two-slice prefetch
-  // running across tile boundaries.  After the last slice of tile t,
-  // epi(t, *this) consumes acc, which is then cleared for the next tile.
+  // a.row0 + t * BM (t = 0 .. ntiles-1), with the prefetch running across tile
+  // boundaries.  After the last slice of tile t, epi(t, *this, free) consumes
+  // acc, which is then cleared; `free` is an LDS stage (kStage bytes) that no
+  // wave reads or loads into until the epilogue returns, when Epi::kUsesLds
+  // asks for it (one extra barrier per tile), else null.
   template <class Epi>
   __device__ __forceinline__ void run_stream(char* lds, const Operand a_op, const Operand b0_op,
                                              const Operand b1_op, bool two_seg, int k_end,
                                              int ntiles, Epi& epi) {
-    const int kt_seg = (k_end + BK - 1) / BK;
+    const int kt_seg = (k_end + kBK - 1) / kBK;
     const int kt_tile = kt_seg * (two_seg ? 2 : 1);
     const int total = kt_tile * ntiles;
     if (total <= 0) return;
     const typename SB::Src b0 = SB::source(b0_op);
     const typename SB::Src b1 = SB::source(two_seg ? b1_op : b0_op);
-    // issue pointer: tile it, slice is within the tile
-    int it = 0, is = 0;
-    auto issue_next = [&](SA& sa, SB& sb) {
-      Operand o = a_op;
-      o.row0 = a_op.row0 + (it < ntiles ? it : ntiles - 1) * BM;
-      const int kt = it < ntiles ? is : kt_tile;       // past the end: out of range
-      issue(sa, sb, SA::source(o), b0, b1, kt_seg, 0, kt);
+    const int past = 2 * kt_seg;
+    // issue pointer: tile it, slice is, its A source and ring stage
+    int it = 0, is = 0, islot = 0;
+    Operand ao = a_op;
+    typename SA::Src a = SA::source(ao);
+    auto issue_next = [&]() {
+      issue(lds + islot * kStage, a, b0, b1, kt_seg, 0, it < ntiles ? is : past);
+      islot = islot == kStages - 1 ? 0 : islot + 1;
       if (++is == kt_tile) {
         is = 0;
-        ++it;
+        if (++it < ntiles) {
+          ao.row0 += BM;
+          a = SA::source(ao);
+        }
       }
     };
-    SA sa0, sa1;
-    SB sb0, sb1;
     zero();
-    issue_next(sa0, sb0);
-    issue_next(sa1, sb1);
-    sa0.store(lds);
-    sb0.store(lds + kLdsA);
-    lds_barrier();
-    int ct = 0, cs = 0;   // compute pointer
-    for (int g = 0; g < total; g += 2) {
-      issue_next(sa0, sb0);
-      __builtin_amdgcn_sched_barrier(0);
-      mma_stage(lds);
-      if (g + 1 < total) {
-        sa1.store(lds + kStage);
-        sb1.store(lds + kStage + kLdsA);
-      }
-      lds_barrier();
+    issue_next();
+    issue_next();
+    int ct = 0, cs = 0, cslot = 0;   // compute pointer
+    for (int g = 0; g < total; ++g) {
+      vm_barrier<kLoads>();
+      issue_next();
+      mma_stage(lds + cslot * kStage);
       if (++cs == kt_tile) {
-        epi(ct, *this);
+        char* free_lds = nullptr;
+        if constexpr (Epi::kUsesLds) {
+          lds_barrier();               // every wave is done reading this stage
+          free_lds = lds + cslot * kStage;
+        }
+        epi(ct, *this, free_lds);
         zero();
         cs = 0;
         ++ct;
       }
-      if (g + 1 >= total) break;
-      issue_next(sa1, sb1);
-      __builtin_amdgcn_sched_barrier(0);
-      mma_stage(lds + kStage);
-      if (g + 2 < total) {
-        sa0.store(lds);
-        sb0.store(lds + kLdsA);
-      }
-      lds_barrier();
-      if (++cs == kt_tile) {
-        epi(ct, *this);
-        zero();
-        cs = 0;
-        ++ct;
-      }
+      cslot = cslot == kStages - 1 ? 0 : cslot + 1;
     }
+    vm_barrier<0>();
   }
 };
 
