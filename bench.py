@@ -34,6 +34,12 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (HBM counter scale)")
+    ap.add_argument("--traffic-record", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR",
+                                                          "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
+                    help="only write profiles/traffic_<kernel>_<workload>.json from rocprofv3 "
+                         "--pmc FETCH_SIZE / WRITE_SIZE output directories of a bench run and of "
+                         "a --copy-calibration-mib run (no GPU needed)")
+    ap.add_argument("--traffic-kernel", default="contract_kernel")
     return ap.parse_args()
 
 
@@ -115,8 +121,70 @@ def _committed_traffic(workload: str, kernel: str):
     return rec.get("bytes_per_launch")
 
 
+def _counter_rows(directory: str, counter: str):
+    import csv
+    import glob
+    rows = []
+    for f in glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True):
+        with open(f, newline="") as fh:
+            rows += [r for r in csv.DictReader(fh) if r["Counter_Name"] == counter]
+    if not rows:
+        raise SystemExit(f"bench.py: no {counter} rows under {directory}")
+    return rows
+
+
+def _per_dispatch_kib(directory: str, counter: str, kernel: str) -> float:
+    vals = [float(r["Counter_Value"]) for r in _counter_rows(directory, counter)
+            if kernel in r["Kernel_Name"]]
+    if not vals:
+        raise SystemExit(f"bench.py: no {kernel} dispatch in {directory}")
+    return sum(vals) / len(vals)
+
+
+def _copy_scale(directory: str, counter: str, copy_bytes: int) -> float:
+    """Bytes moved per counter KiB: the copy kernel moves copy_bytes each way."""
+    vals = [float(r["Counter_Value"]) for r in _counter_rows(directory, counter)
+            if "copyBuffer" in r["Kernel_Name"] or "elementwise" in r["Kernel_Name"].lower()
+            or "copy" in r["Kernel_Name"].lower()]
+    if not vals:
+        raise SystemExit(f"bench.py: no copy kernel in {directory}")
+    scale = copy_bytes / (max(vals) * 1024.0)
+    if not 0.25 <= scale <= 8.0:
+        raise SystemExit(f"bench.py: implausible {counter} scale {scale:.3g} from {directory} "
+                         f"(is it a --copy-calibration-mib {copy_bytes >> 20} run?)")
+    return scale
+
+
+def write_traffic_record(args) -> int:
+    fetch_dir, write_dir, copy_fetch_dir, copy_write_dir = args.traffic_record
+    copy_bytes = (args.copy_calibration_mib or 1024) << 20
+    fetch_kib = _per_dispatch_kib(fetch_dir, "FETCH_SIZE", args.traffic_kernel)
+    write_kib = _per_dispatch_kib(write_dir, "WRITE_SIZE", args.traffic_kernel)
+    fscale = _copy_scale(copy_fetch_dir, "FETCH_SIZE", copy_bytes)
+    wscale = _copy_scale(copy_write_dir, "WRITE_SIZE", copy_bytes)
+    rec = {
+        "workload": args.workload, "kernel": args.traffic_kernel,
+        "source_digest": _source_digest(),
+        "fetch_kib_per_launch": fetch_kib, "write_kib_per_launch": write_kib,
+        "fetch_scale": round(fscale, 3), "write_scale": round(wscale, 3),
+        "bytes_per_launch": fetch_kib * 1024 * fscale + write_kib * 1024 * wscale,
+        "method": "rocprofv3 --pmc FETCH_SIZE, then --pmc WRITE_SIZE, on bench.py --steps 2 "
+                  "--warmup 1 --no-cpu-baseline; KiB per dispatch averaged over launches, each "
+                  "scaled by the same counter's reading for a plain device copy of "
+                  f"{copy_bytes >> 20} MiB (bench.py --copy-calibration-mib)",
+    }
+    path = os.path.join(ROOT, "profiles", f"traffic_{args.traffic_kernel}_{args.workload}.json")
+    with open(path, "w") as fh:
+        json.dump(rec, fh, indent=1)
+        fh.write("\n")
+    print(json.dumps(rec))
+    return 0
+
+
 def main() -> int:
     args = parse()
+    if args.traffic_record:
+        return write_traffic_record(args)
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (got --gpus {args.gpus}); "
               "the path's sharding is described in DESIGN.md", file=sys.stderr)
