@@ -42,7 +42,8 @@ extern "C" {
 
 #define FLCE_OK 0
 #define FLCE_ERR_NULL (-1)      /* a required pointer is null */
-#define FLCE_ERR_SHAPE (-2)     /* N < 0, H < 8, H % 8 != 0, V < 1, or a size too large */
+#define FLCE_ERR_SHAPE (-2)     /* N < 0, H < 8, H % 8 != 0, V < 1, or a size too large:
+                                   N < 2^23, N*H < 2^30, V*H < 2^31, H <= 2^20, V <= 2^30 */
 #define FLCE_ERR_DTYPE (-3)     /* unsupported dtype combination (weight must be bf16) */
 #define FLCE_ERR_ALIGN (-4)     /* a pointer is not aligned as documented */
 #define FLCE_ERR_WORKSPACE (-5) /* workspace smaller than flce_workspace_bytes() */

@@ -25,8 +25,14 @@ int fail(int code, const char* fmt, ...) {
 }
 
 constexpr int64_t kMaxRows = int64_t(1) << 30;
+constexpr int64_t kMaxTokens = (int64_t(1) << 23) - 1;
 constexpr int64_t kMaxHidden = int64_t(1) << 20;
-constexpr int64_t kMaxElems = int64_t(1) << 31;      // N*H and V*H stay int32-indexable per row
+constexpr int64_t kMaxElems = int64_t(1) << 31;      // V*H stays int32-indexable per row
+// Operands read along K address a whole K extent from one buffer descriptor,
+// whose byte size is kept below 2^31 (offsets at 2^31 read zero): a bf16
+// hidden copy (N*H*2 bytes), an lm_head chunk (width*H*2) and a dz chunk
+// (N*width*2) must each stay below it.
+constexpr int64_t kMaxOperandBytes = (int64_t(1) << 31) - 1;
 constexpr size_t kAlign = 256;
 constexpr int64_t kTargetWgs = 2048;                 // ~8 workgroups per CU
 constexpr int64_t kDzWgs = 512;                      // dz workgroups per chunk: one round at two per CU
@@ -50,15 +56,15 @@ struct Plan {
 int validate(const flce_problem* p) {
   if (!p) return fail(FLCE_ERR_NULL, "problem is NULL");
   if (p->reserved != 0) return fail(FLCE_ERR_ARG, "problem.reserved must be 0");
-  if (p->n_tokens < 0 || p->n_tokens > kMaxRows)
-    return fail(FLCE_ERR_SHAPE, "n_tokens=%lld out of range [0, 2^30]", (long long)p->n_tokens);
+  if (p->n_tokens < 0 || p->n_tokens > kMaxTokens)
+    return fail(FLCE_ERR_SHAPE, "n_tokens=%lld out of range [0, 2^23)", (long long)p->n_tokens);
   if (p->vocab < 1 || p->vocab > kMaxRows)
     return fail(FLCE_ERR_SHAPE, "vocab=%lld out of range [1, 2^30]", (long long)p->vocab);
   if (p->hidden < 8 || p->hidden > kMaxHidden || p->hidden % 8 != 0)
     return fail(FLCE_ERR_SHAPE, "hidden=%lld must be a multiple of 8 in [8, 2^20]",
                 (long long)p->hidden);
-  if (p->n_tokens * p->hidden >= kMaxElems || p->vocab * p->hidden >= kMaxElems)
-    return fail(FLCE_ERR_SHAPE, "N*H or V*H exceeds 2^31 elements");
+  if (p->n_tokens * p->hidden * 2 > kMaxOperandBytes || p->vocab * p->hidden >= kMaxElems)
+    return fail(FLCE_ERR_SHAPE, "N*H must stay below 2^30 and V*H below 2^31 elements");
   if (p->hidden_dtype != FLCE_BF16 && p->hidden_dtype != FLCE_F32)
     return fail(FLCE_ERR_DTYPE, "hidden_dtype=%d unsupported (bf16 or fp32)", p->hidden_dtype);
   if (p->weight_dtype != FLCE_BF16)
@@ -86,6 +92,7 @@ Plan make_plan(const flce_problem* p) {
 
   // backward: vocab chunks of about kDzChunkBytes of bf16 dz
   int64_t vc = n > 0 ? (kDzChunkBytes / (2 * n)) / kLogitTileV * kLogitTileV : rup(v, kLogitTileV);
+  vc = std::min<int64_t>(vc, kMaxOperandBytes / (2 * h) / kLogitTileV * kLogitTileV);
   vc = std::max<int64_t>(vc, kLogitTileV);
   vc = std::min<int64_t>(vc, rup(v, kLogitTileV));
   pl.vc = vc;

@@ -63,6 +63,31 @@ def test_small_parity(w):
         check_grad(g["grad_bias"].numpy(), og["grad_bias"], "grad_bias", w.name)
 
 
+def test_lm_head_over_2gib():
+    """An lm_head of more than 2 GiB (262272 x 4096 bf16) with few tokens: the
+    backward's vocabulary chunk is capped so that the lm_head chunk, read along
+    the vocabulary from one buffer descriptor, stays under 2^31 bytes (262016
+    rows, then a 256-row chunk).  Every token against the oracle, grad_hidden
+    whole, grad_weight rows on both sides of the chunk edge and a stride
+    through the first chunk."""
+    w = synth.small_workload(16, 4096, 262272, 1010)
+    say("[parity] lm_head over 2 GiB: drawing inputs")
+    inp = synth.make_inputs(w)
+    say("[parity] lm_head over 2 GiB: running")
+    g = run_gpu(w, inp)
+    h, wt = to_f64(inp.hidden), to_f64(inp.weight)
+    t = inp.targets.numpy()
+    prob = prob_of(w)
+    o = forward(h, wt, None, t, prob)
+    vrows = np.concatenate([np.arange(262016 - 64, 262272), np.arange(0, 262016, 4099)])
+    og = backward(h, wt, None, t, prob, w.reduction, inp.grad_out.numpy(), vocab_rows=vrows)
+    check_tokens(g, o, label=w.name)
+    check_reduced(g, o, label=w.name)
+    check_grad(g["grad_hidden"].numpy(), og["grad_hidden"], "grad_hidden", w.name)
+    check_grad(g["grad_weight"].numpy()[vrows], og["grad_weight_rows"], "grad_weight rows",
+               w.name)
+
+
 def test_num_items_divisor():
     w = synth.small_workload(150, 64, 900, 21)
     say("[parity] num_items divisor")
