@@ -547,22 +547,40 @@ bwd_dz_kernel(const DzArgs a) {
 template <class T>
 __device__ __forceinline__ void store_tile(const T& tile, float* c, int64_t ldc, int m0, int n0,
                                            int m_bound, int n_bound, bool accumulate) {
+  // Rows past m_bound fall outside the descriptor (based at row m0; a tile's
+  // rows stay within 2^31 bytes of it) and read zero / are dropped; columns
+  // past n_bound are sent out of range per lane.  No per-element branch, and
+  // the 16 old values of a 32 x 32 block are loaded together, so an
+  // accumulating store costs one memory round trip per block.
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave & 1, wn = wave >> 1;
+  const __amdgpu_buffer_rsrc_t rs =
+      tile_rsrc(c + (int64_t)m0 * ldc, (int64_t)(m_bound - m0) * ldc * 4);
 #pragma unroll
   for (int i = 0; i < T::TM; ++i)
 #pragma unroll
     for (int j = 0; j < T::TN; ++j) {
       const int n = n0 + wn * (T::kBN / 2) + j * 32 + (lane & 31);
-      if (n >= n_bound) continue;
+      uint32_t off[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int m = m0 + wm * (T::kBM / 2) + i * 32 + acc_row(r, lane);
-        if (m < m_bound) {
-          float* p = c + (int64_t)m * ldc + n;
-          *p = accumulate ? (*p + tile.acc[i][j][r]) : tile.acc[i][j][r];
-        }
+        const int m = wm * (T::kBM / 2) + i * 32 + acc_row(r, lane);
+        off[r] = n < n_bound ? (uint32_t)(m * ldc + n) * 4 : kOutOfRange;
       }
+      float v[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) v[r] = tile.acc[i][j][r];
+      if (accumulate) {
+        float old[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          old[r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, off[r], 0, 0));
+#pragma unroll
+        for (int r = 0; r < 16; ++r) v[r] += old[r];
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v[r]), rs, off[r], 0, 0);
     }
 }
 
