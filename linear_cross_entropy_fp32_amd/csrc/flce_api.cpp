@@ -37,6 +37,7 @@ constexpr size_t kAlign = 256;
 constexpr int64_t kTargetWgs = 2048;                 // ~8 workgroups per CU
 constexpr int64_t kDzWgs = 512;                      // dz workgroups per chunk: one round at two per CU
 constexpr int64_t kDzChunkBytes = int64_t(1) << 28;  // bf16 dz of one backward vocab chunk
+constexpr int64_t kColsumElems = int64_t(1) << 22;   // fp32 partials of the grad_bias sums
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline int64_t rup(int64_t a, int64_t b) { return cdiv(a, b) * b; }
@@ -49,7 +50,8 @@ struct Plan {
   int dz_tiles_per_wg;   // vocab tiles streamed by one dz workgroup
   int gh_splits;         // split-K of the grad_hidden contraction
   int64_t gh_kps;
-  size_t off_hsplit, off_part, off_bsums, off_dz, off_ghpart;
+  int cs_segs;           // row segments of the grad_bias column sums
+  size_t off_hsplit, off_part, off_bsums, off_dz, off_ghpart, off_cspart;
   size_t fwd_bytes, bwd_bytes, bytes;
 };
 
@@ -122,6 +124,9 @@ Plan make_plan(const flce_problem* p) {
   off += aup(size_t(n) * vc * 2);
   pl.off_ghpart = off;
   if (pl.gh_splits > 1) off += aup(size_t(pl.gh_splits) * n * h * 4);
+  pl.cs_segs = (int)std::max<int64_t>(1, std::min<int64_t>(cdiv(n, 256), kColsumElems / vc));
+  pl.off_cspart = off;
+  off += aup(size_t(pl.cs_segs) * vc * 4);
   pl.bwd_bytes = off;
   pl.bytes = std::max(pl.fwd_bytes, pl.bwd_bytes);
   return pl;
@@ -396,7 +401,10 @@ int flce_backward(const flce_problem* p, const void* hidden, const void* weight,
       return rc;
 
     if (grad_bias &&
-        (rc = hip_check(launch_colsum(dz, pl.vc, (int)n, (int)width, grad_bias + c0, s), "colsum")))
+        (rc = hip_check(launch_colsum(dz, pl.vc, (int)n, (int)width, pl.cs_segs,
+                                      reinterpret_cast<float*>(ws + pl.off_cspart),
+                                      grad_bias + c0, s),
+                        "colsum")))
       return rc;
   }
   if (pl.gh_splits > 1 &&

@@ -101,8 +101,9 @@ hipError_t launch_bwd_dz(const DzArgs& a, bool cap, hipStream_t s);
 hipError_t launch_contract(const ContractArgs& a, hipStream_t s);
 hipError_t launch_sum_partials(const float* part, int nsplit, int64_t stride, float* out,
                                int64_t count, hipStream_t s);
-hipError_t launch_colsum(const uint16_t* dz, int64_t ldz, int n_tok, int width, float* out,
-                         hipStream_t s);
+// grad_bias of one chunk; part: nseg * width floats of workspace.
+hipError_t launch_colsum(const uint16_t* dz, int64_t ldz, int n_tok, int width, int nseg,
+                         float* part, float* out, hipStream_t s);
 hipError_t launch_fill_zero(float* p, int64_t count, hipStream_t s);
 
 }  // namespace flce

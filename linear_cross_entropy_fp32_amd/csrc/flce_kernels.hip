@@ -35,6 +35,7 @@ using GwTile = Tile<kGemmTileM, kGemmTileN, false, false>;         // dz^T . h
 constexpr int kColumns = LogitTile::TN;      // token columns per lane
 constexpr int kQ = LogitTile::TM * 16;       // values per token column per lane
 constexpr int kWaveRows = kLogitTileV / 2;   // vocabulary rows per wave
+constexpr int kGroupBand = 8;                // vocabulary groups per band of grouped_order
 
 // ------------------------------------------------------------------ helpers
 
@@ -258,8 +259,9 @@ template <bool CAP, bool FIXED, bool BIAS>
 __global__ void __launch_bounds__(kThreads, 2)
 fwd_stats_kernel(const FwdArgs a) {
   __shared__ __attribute__((aligned(16))) char lds[LogitTile::kLdsBytes];
-  const int bid = xcd_remap(blockIdx.x, gridDim.x);
-  const int tt = bid % a.n_tok_tiles, sp = bid / a.n_tok_tiles;
+  const GridPos gp = grouped_order(xcd_remap(blockIdx.x, gridDim.x), a.n_tok_tiles, a.n_splits,
+                                   kGroupBand);
+  const int tt = gp.tt, sp = gp.grp;
   const int n0 = tt * kLogitTileN;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave & 1, wn = wave >> 1;
@@ -512,8 +514,10 @@ template <bool CAP, bool BIAS>
 __global__ void __launch_bounds__(kThreads, 2)
 bwd_dz_kernel(const DzArgs a) {
   __shared__ __attribute__((aligned(16))) char lds[LogitTile::kLdsBytes];
-  const int bid = xcd_remap(blockIdx.x, gridDim.x);
-  const int tt = bid % a.n_tok_tiles, grp = bid / a.n_tok_tiles;
+  const int groups = (a.chunk_tiles + a.tiles_per_wg - 1) / a.tiles_per_wg;
+  const GridPos gp = grouped_order(xcd_remap(blockIdx.x, gridDim.x), a.n_tok_tiles, groups,
+                                   kGroupBand);
+  const int tt = gp.tt, grp = gp.grp;
   const int n0 = tt * kLogitTileN;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave & 1, wn = wave >> 1;
@@ -635,19 +639,49 @@ __global__ void sum_partials_kernel(const float* __restrict__ part, int nsplit, 
   out[i] = s;
 }
 
-// gb[c0 + v] = sum_n dz[n, v] for one chunk (fp32 accumulation of bf16 dz).
-__global__ void colsum_kernel(const uint16_t* __restrict__ dz, int64_t ldz, int n_tok,
-                              int width, float* __restrict__ out) {
+// grad_bias of one chunk, gb[v] = sum_n dz[n, v] (fp32 accumulation of the bf16
+// dz), in two fixed-order passes.  Pass 1: block (column block of 512, row
+// segment) has 64 column groups of 8 columns x 4 row phases; each thread
+// sums its rows with 16-byte loads, the 4 phases are added in order in LDS,
+// and the block writes part[seg][512 columns].  Pass 2 adds the segments in
+// order.
+constexpr int kColBlock = 512;
+__global__ void __launch_bounds__(256)
+colsum_partial_kernel(const uint16_t* __restrict__ dz, int64_t ldz, int n_tok, int width,
+                      int rows_per_seg, float* __restrict__ part) {
+  const int cg = threadIdx.x & 63, ph = threadIdx.x >> 6;
+  const int c0 = blockIdx.x * kColBlock + cg * 8;
+  const int seg = blockIdx.y;
+  const int r0 = seg * rows_per_seg, r1 = min(n_tok, r0 + rows_per_seg);
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  if (c0 < width) {
+    for (int n = r0 + ph; n < r1; n += 4) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(dz + (int64_t)n * ldz + c0);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[2 * e] += __builtin_bit_cast(float, v[e] << 16);
+        acc[2 * e + 1] += __builtin_bit_cast(float, v[e] & 0xffff0000u);
+      }
+    }
+  }
+  __shared__ float red[4][kColBlock];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) red[ph][cg * 8 + e] = acc[e];
+  __syncthreads();
+  for (int c = threadIdx.x; c < kColBlock; c += 256) {
+    const int col = blockIdx.x * kColBlock + c;
+    if (col < width)
+      part[(int64_t)seg * width + col] = ((red[0][c] + red[1][c]) + red[2][c]) + red[3][c];
+  }
+}
+
+__global__ void colsum_reduce_kernel(const float* __restrict__ part, int nseg, int width,
+                                     float* __restrict__ out) {
   const int v = blockIdx.x * blockDim.x + threadIdx.x;
   if (v >= width) return;
-  float s0 = 0.f, s1 = 0.f;
-  int n = 0;
-  for (; n + 1 < n_tok; n += 2) {
-    s0 += __builtin_bit_cast(float, (uint32_t)dz[(int64_t)n * ldz + v] << 16);
-    s1 += __builtin_bit_cast(float, (uint32_t)dz[(int64_t)(n + 1) * ldz + v] << 16);
-  }
-  if (n < n_tok) s0 += __builtin_bit_cast(float, (uint32_t)dz[(int64_t)n * ldz + v] << 16);
-  out[v] = s0 + s1;
+  float s = part[v];
+  for (int g = 1; g < nseg; ++g) s += part[(int64_t)g * width + v];
+  out[v] = s;
 }
 
 __global__ void fill_zero_kernel(float* __restrict__ p, int64_t count) {
@@ -721,10 +755,15 @@ hipError_t launch_sum_partials(const float* part, int nsplit, int64_t stride, fl
   return hipGetLastError();
 }
 
-hipError_t launch_colsum(const uint16_t* dz, int64_t ldz, int n_tok, int width, float* out,
-                         hipStream_t s) {
+hipError_t launch_colsum(const uint16_t* dz, int64_t ldz, int n_tok, int width, int nseg,
+                         float* part, float* out, hipStream_t s) {
   if (width == 0) return hipSuccess;
-  colsum_kernel<<<grid1(width, 256), 256, 0, s>>>(dz, ldz, n_tok, width, out);
+  if (n_tok == 0) return launch_fill_zero(out, width, s);
+  const int rows_per_seg = (n_tok + nseg - 1) / nseg;
+  nseg = (n_tok + rows_per_seg - 1) / rows_per_seg;
+  const dim3 grid((unsigned)((width + kColBlock - 1) / kColBlock), (unsigned)nseg);
+  colsum_partial_kernel<<<grid, 256, 0, s>>>(dz, ldz, n_tok, width, rows_per_seg, part);
+  colsum_reduce_kernel<<<grid1(width, 256), 256, 0, s>>>(part, nseg, width, out);
   return hipGetLastError();
 }
 

@@ -373,6 +373,21 @@ struct Tile {
   }
 };
 
+// Grouped order over a (token tile, vocabulary group) grid: consecutive ids
+// walk a column of `gh` groups for one token tile, then the next token tile,
+// so a run of 64 ids (what one XCD holds at once at two workgroups per CU)
+// covers 64 / gh token tiles x gh groups and each operand tile is read by
+// several resident workgroups out of L2.  The last band may hold fewer groups.
+struct GridPos {
+  int tt, grp;
+};
+__device__ __forceinline__ GridPos grouped_order(int id, int n_tt, int n_grp, int band) {
+  const int per_band = n_tt * band;
+  const int b = id / per_band, r = id - b * per_band;
+  const int gh = min(band, n_grp - b * band);
+  return GridPos{r / gh, b * band + r % gh};
+}
+
 // Map a linear workgroup id so that ids adjacent in the logical order land on
 // the same XCD (workgroups are dealt to the 8 XCDs round robin), keeping tiles
 // that share an operand in one L2.
