@@ -38,6 +38,7 @@ constexpr int64_t kTargetWgs = 2048;                 // ~8 workgroups per CU
 constexpr int64_t kDzWgs = 512;                      // dz workgroups per chunk: one round at two per CU
 constexpr int64_t kDzChunkBytes = int64_t(1) << 28;  // bf16 dz of one backward vocab chunk
 constexpr int64_t kColsumElems = int64_t(1) << 22;   // fp32 partials of the grad_bias sums
+constexpr int64_t kL2Bytes = int64_t(4) << 20;        // L2 of one XCD
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline int64_t rup(int64_t a, int64_t b) { return cdiv(a, b) * b; }
@@ -51,6 +52,8 @@ struct Plan {
   int gh_splits;         // split-K of the grad_hidden contraction
   int64_t gh_kps;
   int cs_segs;           // row segments of the grad_bias column sums
+  int tt_fastest;        // logit-tile workgroup order: token tile fastest when
+                         // the bf16 hidden operand fits in one XCD's L2
   size_t off_hsplit, off_part, off_bsums, off_dz, off_ghpart, off_cspart;
   size_t fwd_bytes, bwd_bytes, bytes;
 };
@@ -91,6 +94,8 @@ Plan make_plan(const flce_problem* p) {
   pl.tiles_per_split = (int)cdiv(pl.n_voc_tiles, splits);
   pl.n_splits = (int)cdiv(pl.n_voc_tiles, pl.tiles_per_split);
   pl.fin_blocks = (int)cdiv(n, 32);
+  const int64_t hidden_bf16_bytes = n * h * 2 * (p->hidden_dtype == FLCE_F32 ? 2 : 1);
+  pl.tt_fastest = hidden_bf16_bytes <= kL2Bytes ? 1 : 0;
 
   // backward: vocab chunks of about kDzChunkBytes of bf16 dz
   int64_t vc = n > 0 ? (kDzChunkBytes / (2 * n)) / kLogitTileV * kLogitTileV : rup(v, kLogitTileV);
@@ -266,6 +271,7 @@ int flce_forward(const flce_problem* p, const void* hidden, const void* weight,
     logit_consts(p, a.kx, a.c1, a.c2);
     a.n_tok_tiles = pl.n_tok_tiles;
     a.n_splits = pl.n_splits;
+    a.tt_fastest = pl.tt_fastest;
     a.tiles_per_split = pl.tiles_per_split;
     a.n_voc_tiles = pl.n_voc_tiles;
     a.part = part;
@@ -364,6 +370,7 @@ int flce_backward(const flce_problem* p, const void* hidden, const void* weight,
   d.ignore_index = p->ignore_index;
   logit_consts(p, d.kx, d.c1, d.c2);
   d.n_tok_tiles = pl.n_tok_tiles;
+  d.tt_fastest = pl.tt_fastest;
   d.tiles_per_wg = pl.dz_tiles_per_wg;
   d.dz = dz;
   d.ldz = pl.vc;

@@ -38,6 +38,7 @@ struct FwdArgs {
   int n, hdim, v;
   float kx, c1, c2;      // see final_u()
   int n_tok_tiles, n_splits, tiles_per_split, n_voc_tiles;
+  int tt_fastest;        // workgroup order (see grouped_order)
   PartState* part;       // [n_splits, N]
 };
 
@@ -73,6 +74,7 @@ struct DzArgs {
   int chunk_tiles;       // vocab tiles in the chunk
   int tiles_per_wg;      // vocab tiles streamed by one workgroup
   int n_tok_tiles;
+  int tt_fastest;        // workgroup order (see grouped_order)
   uint16_t* dz;          // [N, ldz] bf16 chunk buffer
   int64_t ldz;
 };

@@ -35,7 +35,6 @@ using GwTile = Tile<kGemmTileM, kGemmTileN, false, false>;         // dz^T . h
 constexpr int kColumns = LogitTile::TN;      // token columns per lane
 constexpr int kQ = LogitTile::TM * 16;       // values per token column per lane
 constexpr int kWaveRows = kLogitTileV / 2;   // vocabulary rows per wave
-constexpr int kGroupBand = 8;                // vocabulary groups per band of grouped_order
 
 // ------------------------------------------------------------------ helpers
 
@@ -259,8 +258,8 @@ template <bool CAP, bool FIXED, bool BIAS>
 __global__ void __launch_bounds__(kThreads, 2)
 fwd_stats_kernel(const FwdArgs a) {
   __shared__ __attribute__((aligned(16))) char lds[LogitTile::kLdsBytes];
-  const GridPos gp = grouped_order(xcd_remap(blockIdx.x, gridDim.x), a.n_tok_tiles, a.n_splits,
-                                   kGroupBand);
+  const GridPos gp =
+      grouped_order(xcd_remap(blockIdx.x, gridDim.x), a.n_tok_tiles, a.n_splits, a.tt_fastest);
   const int tt = gp.tt, sp = gp.grp;
   const int n0 = tt * kLogitTileN;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -515,8 +514,8 @@ __global__ void __launch_bounds__(kThreads, 2)
 bwd_dz_kernel(const DzArgs a) {
   __shared__ __attribute__((aligned(16))) char lds[LogitTile::kLdsBytes];
   const int groups = (a.chunk_tiles + a.tiles_per_wg - 1) / a.tiles_per_wg;
-  const GridPos gp = grouped_order(xcd_remap(blockIdx.x, gridDim.x), a.n_tok_tiles, groups,
-                                   kGroupBand);
+  const GridPos gp =
+      grouped_order(xcd_remap(blockIdx.x, gridDim.x), a.n_tok_tiles, groups, a.tt_fastest);
   const int tt = gp.tt, grp = gp.grp;
   const int n0 = tt * kLogitTileN;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;

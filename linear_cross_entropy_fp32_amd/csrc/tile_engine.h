@@ -373,19 +373,25 @@ struct Tile {
   }
 };
 
-// Grouped order over a (token tile, vocabulary group) grid: consecutive ids
-// walk a column of `gh` groups for one token tile, then the next token tile,
-// so a run of 64 ids (what one XCD holds at once at two workgroups per CU)
-// covers 64 / gh token tiles x gh groups and each operand tile is read by
-// several resident workgroups out of L2.  The last band may hold fewer groups.
+// Order over a (token tile, vocabulary group) grid in windows of up to
+// G groups x T token tiles (G = T = 8: 64 workgroups, what one XCD holds at
+// two per CU).  Inside a window, consecutive workgroups share the operand
+// that benefits most from being read by workgroups that run in step: the
+// vocabulary group (token tile fastest) when all token tiles fit in L2
+// anyway, else the token tile (group fastest).  Windows run over the token
+// tiles of a band of G groups, then the next band; edge windows are
+// narrower.  The map is a bijection onto the n_tt x n_grp grid.
 struct GridPos {
   int tt, grp;
 };
-__device__ __forceinline__ GridPos grouped_order(int id, int n_tt, int n_grp, int band) {
-  const int per_band = n_tt * band;
-  const int b = id / per_band, r = id - b * per_band;
-  const int gh = min(band, n_grp - b * band);
-  return GridPos{r / gh, b * band + r % gh};
+__device__ __forceinline__ GridPos grouped_order(int id, int n_tt, int n_grp, bool tt_fastest) {
+  constexpr int G = 8, T = 8;
+  const int b = id / (n_tt * G), r = id - b * (n_tt * G);
+  const int gh = min(G, n_grp - b * G);              // groups in this band
+  const int tb = r / (T * gh), j = r - tb * (T * gh);
+  const int tw = min(T, n_tt - tb * T);              // token tiles in this window
+  return tt_fastest ? GridPos{tb * T + j % tw, b * G + j / tw}
+                    : GridPos{tb * T + j / gh, b * G + j % gh};
 }
 
 // Map a linear workgroup id so that ids adjacent in the logical order land on
