@@ -259,6 +259,9 @@ struct Tile {
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
   }
 
+  // One slice.  FIRST: the slice starts a tile, so its first MFMAs take a
+  // zero accumulator input instead of the registers being cleared.
+  template <bool FIRST = false>
   __device__ __forceinline__ void mma_stage(const char* lds) {
     const int wave = threadIdx.x >> 6;
     const int wm = wave & 1, wn = wave >> 1;
@@ -272,8 +275,14 @@ struct Tile {
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < TN; ++j) {
+          if (FIRST && ks == 0) {
+            const f32x16 z = {};
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], z, 0, 0, 0);
+          } else {
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+          }
+        }
     }
   }
 
@@ -290,8 +299,9 @@ struct Tile {
     SB::issue(seg ? b1 : b0, buf + kLdsA, k0);
   }
 
-  // Accumulate over k in [k_begin, k_end), or twice over it when two_seg is
-  // set (A against b0, then against b1).  The range is read in whole slices:
+  // acc = the sum over k in [k_begin, k_end), or twice over it when two_seg
+  // is set (A against b0, then against b1); acc is overwritten (an empty
+  // range leaves it untouched).  The range is read in whole slices:
   // k_end - k_begin must be a multiple of 32 unless k_end is the operands' K
   // bound (past which loads read zero).
   __device__ __forceinline__ void run(char* lds, const Operand a_op, const Operand b0_op,
@@ -306,7 +316,13 @@ struct Tile {
     issue(lds, a, b0, b1, kt_seg, k_begin, 0);
     issue(lds + kStage, a, b0, b1, kt_seg, k_begin, kt_total > 1 ? 1 : past);
     int slot = 0, nslot = 2;
-    for (int kt = 0; kt < kt_total; ++kt) {
+    // slice 0 starts the accumulators from zero
+    vm_barrier<kLoads>();
+    issue(lds + nslot * kStage, a, b0, b1, kt_seg, k_begin, kt_total > 2 ? 2 : past);
+    mma_stage<true>(lds);
+    slot = 1;
+    nslot = 0;
+    for (int kt = 1; kt < kt_total; ++kt) {
       vm_barrier<kLoads>();            // slice kt landed; slice kt-1 no longer read
       issue(lds + nslot * kStage, a, b0, b1, kt_seg, k_begin, kt + 2 < kt_total ? kt + 2 : past);
       mma_stage(lds + slot * kStage);
@@ -319,7 +335,7 @@ struct Tile {
   // Streams `ntiles` tiles that share the B operand and take A rows
   // a.row0 + t * BM (t = 0 .. ntiles-1), with the prefetch running across tile
   // boundaries.  After the last slice of tile t, epi(t, *this, free) consumes
-  // acc, which is then cleared; `free` is an LDS stage (kStage bytes) that no
+  // acc (the next tile starts from zero again); `free` is an LDS stage (kStage bytes) that no
   // wave reads or loads into until the epilogue returns, when Epi::kUsesLds
   // asks for it (one extra barrier per tile), else null.
   template <class Epi>
@@ -328,8 +344,7 @@ struct Tile {
                                              int ntiles, Epi& epi) {
     const int kt_seg = (k_end + kBK - 1) / kBK;
     const int kt_tile = kt_seg * (two_seg ? 2 : 1);
-    const int total = kt_tile * ntiles;
-    if (total <= 0) return;
+    if (kt_tile <= 0 || ntiles <= 0) return;
     const typename SB::Src b0 = SB::source(b0_op);
     const typename SB::Src b1 = SB::source(two_seg ? b1_op : b0_op);
     const int past = 2 * kt_seg;
@@ -348,25 +363,27 @@ struct Tile {
         }
       }
     };
-    zero();
     issue_next();
     issue_next();
-    int ct = 0, cs = 0, cslot = 0;   // compute pointer
-    for (int g = 0; g < total; ++g) {
+    int cslot = 0;   // ring stage being multiplied
+    for (int ct = 0; ct < ntiles; ++ct) {
+      // the first slice of a tile starts the accumulators from zero, so they
+      // are dead between the previous epilogue and here
       vm_barrier<kLoads>();
       issue_next();
-      mma_stage(lds + cslot * kStage);
-      if (++cs == kt_tile) {
-        char* free_lds = nullptr;
-        if constexpr (Epi::kUsesLds) {
-          lds_barrier();               // every wave is done reading this stage
-          free_lds = lds + cslot * kStage;
-        }
-        epi(ct, *this, free_lds);
-        zero();
-        cs = 0;
-        ++ct;
+      mma_stage<true>(lds + cslot * kStage);
+      for (int cs = 1; cs < kt_tile; ++cs) {
+        cslot = cslot == kStages - 1 ? 0 : cslot + 1;
+        vm_barrier<kLoads>();
+        issue_next();
+        mma_stage(lds + cslot * kStage);
       }
+      char* free_lds = nullptr;
+      if constexpr (Epi::kUsesLds) {
+        lds_barrier();                 // every wave is done reading this stage
+        free_lds = lds + cslot * kStage;
+      }
+      epi(ct, *this, free_lds);
       cslot = cslot == kStages - 1 ? 0 : cslot + 1;
     }
     vm_barrier<0>();
