@@ -46,6 +46,9 @@ SMALL = [
     synth.small_workload(96, 512, 1500, 17, hidden_dtype="f32", softcap=30.0),
     synth.small_workload(64, 128, 1, 18),                                # V = 1
     synth.small_workload(70, 64, 2, 19, bias=True),                      # V = 2
+    # softcap above 120 / (2 log2 e): the forward keeps a running reference
+    synth.small_workload(180, 96, 2100, 24, softcap=50.0, logit_scale=20.0, bias=True),
+    synth.small_workload(300, 64, 1700, 25, softcap=60.0, logit_scale=8.0, reduction="none"),
 ]
 
 
@@ -110,6 +113,28 @@ def test_all_ignored_small_is_exactly_zero():
     assert g["reduced_i64"].numpy().tolist() == [0, 0, 0]
     for k in ("grad_hidden", "grad_weight", "grad_bias"):
         assert torch.count_nonzero(g[k]).item() == 0, k
+
+
+@pytest.mark.parametrize("softcap", [0.0, 30.0, 50.0])
+def test_zero_lm_head_ties(softcap):
+    """lm_head = 0 and no bias: every logit is 0, so the loss and the entropy
+    are ln V exactly, the argmax is the lowest index (0) on every row across
+    all vocabulary splits, grad_hidden is 0 and grad_weight[v] = sum_n g_n
+    (1/V - [t_n = v]) h_n (oracle)."""
+    w = synth.small_workload(260, 64, 5003, 26, softcap=softcap)
+    inp = synth.make_inputs(w)
+    inp.weight.zero_()
+    say(f"[parity] zero lm_head, softcap {softcap}")
+    g = run_gpu(w, inp)
+    valid = inp.targets.numpy() != -100
+    ln_v = float(np.log(5003.0))
+    assert np.abs(g["loss"].numpy()[valid] - ln_v).max() <= 2e-3
+    assert np.abs(g["entropy"].numpy()[valid] - ln_v).max() <= 2e-3
+    assert np.all(g["argmax"].numpy() == 0)
+    assert np.array_equal(g["hit"].numpy().astype(bool), valid & (inp.targets.numpy() == 0))
+    assert torch.count_nonzero(g["grad_hidden"]).item() == 0
+    o, og = _oracle_all(w, inp)
+    check_grad(g["grad_weight"].numpy(), og["grad_weight"], "grad_weight", "zero lm_head")
 
 
 def test_bad_targets_counted():
