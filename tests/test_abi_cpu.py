@@ -152,3 +152,18 @@ def test_binding_requires_targets_and_reduction():
         flce.linear_cross_entropy(h, w, None)
     with pytest.raises(ValueError):
         flce.linear_cross_entropy(h, w, torch.zeros(4, dtype=torch.int64), reduction="avg")
+
+
+def test_timing_hook_arguments():
+    """The benchmark timing hook rejects bad requests and reports how many
+    launches it recorded under the previous setting (none here: no launch
+    happens without a GPU)."""
+    lib = flce.lib()
+    events = (ctypes.c_void_p * 2)()
+    assert lib.flce_set_timing_events(7, events, 1) == -7
+    assert lib.flce_set_timing_events(-1, events, 1) == -7
+    assert lib.flce_set_timing_events(flce.FLCE_KERNEL_CONTRACT, events, -1) == -7
+    assert lib.flce_set_timing_events(flce.FLCE_KERNEL_CONTRACT, None, 1) == -7
+    assert lib.flce_set_timing_events(flce.FLCE_KERNEL_CONTRACT, events, 1) == 0
+    assert lib.flce_set_timing_events(flce.FLCE_KERNEL_CONTRACT, None, 0) == 0
+

@@ -137,6 +137,39 @@ def test_zero_lm_head_ties(softcap):
     check_grad(g["grad_weight"].numpy(), og["grad_weight"], "grad_weight", "zero lm_head")
 
 
+def test_timing_hook_records_each_launch():
+    """flce_set_timing_events brackets every launch of the chosen kernel: a
+    backward over 40000 vocabulary rows with 4100 tokens runs two vocabulary
+    chunks (as the planning rule gives), hence two contraction launches, each
+    with a positive duration."""
+    import ctypes
+    w = synth.small_workload(4100, 128, 40000, 16)
+    inp = synth.make_inputs(w)
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipEventCreate.argtypes = [ctypes.c_void_p]
+    hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                        ctypes.c_void_p]
+    hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    evs = (ctypes.c_void_p * 8)()
+    for i in range(8):
+        assert hip.hipEventCreate(ctypes.byref(evs, i * ctypes.sizeof(ctypes.c_void_p))) == 0
+    say("[parity] timing hook")
+    try:
+        flce.flce_set_timing_events(flce.FLCE_KERNEL_CONTRACT, evs, 4)
+        run_gpu(w, inp)
+        recorded = flce.flce_set_timing_events(flce.FLCE_KERNEL_CONTRACT, None, 0)
+        assert recorded == 2, recorded
+        for i in range(recorded):
+            ms = ctypes.c_float(0.0)
+            assert hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(evs[2 * i]),
+                                           ctypes.c_void_p(evs[2 * i + 1])) == 0
+            assert ms.value > 0.0
+    finally:
+        flce.flce_set_timing_events(flce.FLCE_KERNEL_CONTRACT, None, 0)
+        for i in range(8):
+            hip.hipEventDestroy(ctypes.c_void_p(evs[i]))
+
+
 def test_bad_targets_counted():
     w = synth.small_workload(200, 64, 500, 23)
     inp = synth.make_inputs(w)
