@@ -89,10 +89,13 @@ def _hip_ok(rc: int) -> None:
 
 
 def _chunks_per_backward(prob) -> int:
-    """Upper bound on contraction launches per backward: one per vocab chunk of
-    at most 2^28 bytes of bf16 dz (the library's own planning is finer)."""
+    """Upper bound on contraction launches per backward: one per vocab chunk,
+    and no chunk is narrower than 2^27 bytes of bf16 dz per token row allows,
+    nor than the 2^31-byte limit on one lm_head chunk allows (128-row units)."""
     n = max(1, prob.n_tokens)
-    rows = max(128, ((1 << 28) // (2 * n)) // 128 * 128)
+    rows = ((1 << 27) // (2 * n)) // 128 * 128
+    rows = min(rows, ((1 << 31) - 1) // (2 * max(1, prob.hidden)) // 128 * 128)
+    rows = max(128, rows)
     return max(1, -(-prob.vocab // rows))
 
 
@@ -253,7 +256,7 @@ def main() -> int:
     # the launch stream (flce_set_timing_events) over the whole timed region
     hip = _hip_runtime()
     n_chunks = _chunks_per_backward(prob)
-    n_pairs = args.steps * n_chunks
+    n_pairs = args.steps * n_chunks + 1      # one spare pair: a full pool means overflow
     evs = (ctypes.c_void_p * (2 * n_pairs))()
     for i in range(2 * n_pairs):
         _hip_ok(hip.hipEventCreate(ctypes.byref(evs, i * ctypes.sizeof(ctypes.c_void_p))))
@@ -275,6 +278,9 @@ def main() -> int:
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall
     recorded = flce.flce_set_timing_events(_binding.FLCE_KERNEL_CONTRACT, None, 0)
+    if recorded >= n_pairs:
+        raise RuntimeError("more contraction launches than timing events: the per-step "
+                           "kernel time would be incomplete")
     kern_ms = []
     for i in range(recorded):
         ms_i = ctypes.c_float(0.0)

@@ -36,7 +36,15 @@ constexpr int64_t kMaxOperandBytes = (int64_t(1) << 31) - 1;
 constexpr size_t kAlign = 256;
 constexpr int64_t kTargetWgs = 2048;                 // ~8 workgroups per CU
 constexpr int64_t kDzWgs = 512;                      // dz workgroups per chunk: one round at two per CU
-constexpr int64_t kDzChunkBytes = int64_t(1) << 28;  // bf16 dz of one backward vocab chunk
+// bf16 dz of one backward vocab chunk.  A 128 MiB chunk stays in the 256 MB
+// last-level cache (MALL) between the dz write and the contraction's two
+// reads of it; it is used while it leaves the chunk at least kMinChunkWidth
+// vocab rows wide, since narrower chunks unbalance the contraction (few long
+// grad_weight tiles against many short grad_hidden ones).  Otherwise the
+// chunk is 256 MiB.
+constexpr int64_t kDzChunkBytes = int64_t(1) << 27;
+constexpr int64_t kDzChunkBytesWide = int64_t(1) << 28;
+constexpr int64_t kMinChunkWidth = 8192;
 constexpr int64_t kColsumElems = int64_t(1) << 22;   // fp32 partials of the grad_bias sums
 constexpr int64_t kL2Bytes = int64_t(4) << 20;        // L2 of one XCD
 
@@ -97,8 +105,11 @@ Plan make_plan(const flce_problem* p) {
   const int64_t hidden_bf16_bytes = n * h * 2 * (p->hidden_dtype == FLCE_F32 ? 2 : 1);
   pl.tt_fastest = hidden_bf16_bytes <= kL2Bytes ? 1 : 0;
 
-  // backward: vocab chunks of about kDzChunkBytes of bf16 dz
+  // backward: vocab chunks of about kDzChunkBytes of bf16 dz, or of
+  // kDzChunkBytesWide when the former would be narrower than kMinChunkWidth
   int64_t vc = n > 0 ? (kDzChunkBytes / (2 * n)) / kLogitTileV * kLogitTileV : rup(v, kLogitTileV);
+  if (n > 0 && vc < kMinChunkWidth)
+    vc = (kDzChunkBytesWide / (2 * n)) / kLogitTileV * kLogitTileV;
   vc = std::min<int64_t>(vc, kMaxOperandBytes / (2 * h) / kLogitTileV * kLogitTileV);
   vc = std::max<int64_t>(vc, kLogitTileV);
   vc = std::min<int64_t>(vc, rup(v, kLogitTileV));

@@ -42,7 +42,7 @@ SMALL = [
     synth.small_workload(333, 128, 2500, 14, logit_scale=0.0625, targets="zipf",
                          reduction="sum"),
     synth.small_workload(200, 256, 3001, 15, softcap=5.0, reduction="none", bias=True),
-    synth.small_workload(4100, 128, 40000, 16, reduction="mean"),       # two vocab chunks
+    synth.small_workload(4100, 128, 40000, 16, reduction="mean"),       # three vocab chunks, the last ragged
     synth.small_workload(96, 512, 1500, 17, hidden_dtype="f32", softcap=30.0),
     synth.small_workload(64, 128, 1, 18),                                # V = 1
     synth.small_workload(70, 64, 2, 19, bias=True),                      # V = 2
@@ -139,11 +139,12 @@ def test_zero_lm_head_ties(softcap):
 
 def test_timing_hook_records_each_launch():
     """flce_set_timing_events brackets every launch of the chosen kernel: a
-    backward over 40000 vocabulary rows with 4100 tokens runs two vocabulary
-    chunks (as the planning rule gives), hence two contraction launches, each
-    with a positive duration."""
+    backward over 30000 vocabulary rows with 4100 tokens runs two vocabulary
+    chunks (the planning rule gives chunks of 16256 rows: 2^27 bytes of bf16 dz
+    per chunk, rounded down to 128-row tiles), hence two contraction launches,
+    each with a positive duration."""
     import ctypes
-    w = synth.small_workload(4100, 128, 40000, 16)
+    w = synth.small_workload(4100, 128, 30000, 16)
     inp = synth.make_inputs(w)
     hip = ctypes.CDLL("libamdhip64.so")
     hip.hipEventCreate.argtypes = [ctypes.c_void_p]
