@@ -74,9 +74,17 @@ def cpu_baseline(w, inp, budget_s: float) -> dict:
                       f"(float64 numpy), {dt:.1f} s"}
 
 
+# Timing-only events: no system-scope fence (cache writeback and invalidate)
+# when an event is recorded, so that recording one between two kernels does
+# not open a gap between them (HIP's hipEventDisableSystemFence).
+_EVENT_TIMING_ONLY = 0x20000000
+
+
 def _hip_runtime():
     hip = ctypes.CDLL("libamdhip64.so")
     hip.hipEventCreate.argtypes = [ctypes.c_void_p]
+    hip.hipEventCreateWithFlags.argtypes = [ctypes.c_void_p, ctypes.c_uint]
+    hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
     hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
                                         ctypes.c_void_p]
     hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
@@ -253,27 +261,38 @@ def main() -> int:
     torch.cuda.synchronize()
 
     # HIP events for the dominant kernel's launches, recorded by the library on
-    # the launch stream (flce_set_timing_events) over the whole timed region
+    # the launch stream (flce_set_timing_events) over the whole timed region,
+    # and for the forward / backward split of every step; all timing-only
     hip = _hip_runtime()
     n_chunks = _chunks_per_backward(prob)
     n_pairs = args.steps * n_chunks + 1      # one spare pair: a full pool means overflow
-    evs = (ctypes.c_void_p * (2 * n_pairs))()
-    for i in range(2 * n_pairs):
-        _hip_ok(hip.hipEventCreate(ctypes.byref(evs, i * ctypes.sizeof(ctypes.c_void_p))))
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
-           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    n_step_ev = 3 * args.steps
+    evs = (ctypes.c_void_p * (2 * n_pairs + n_step_ev))()
+    for i in range(2 * n_pairs + n_step_ev):
+        _hip_ok(hip.hipEventCreateWithFlags(ctypes.byref(evs, i * ctypes.sizeof(ctypes.c_void_p)),
+                                            _EVENT_TIMING_ONLY))
+    step_ev = [evs[2 * n_pairs + i] for i in range(n_step_ev)]
+
+    def elapsed(a, b):
+        ms_i = ctypes.c_float(0.0)
+        _hip_ok(hip.hipEventElapsedTime(ctypes.byref(ms_i), ctypes.c_void_p(a), ctypes.c_void_p(b)))
+        return ms_i.value
+
+    def mark(e):
+        _hip_ok(hip.hipEventRecord(ctypes.c_void_p(e), sp))
+
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
     flce.flce_set_timing_events(_binding.FLCE_KERNEL_CONTRACT, evs, n_pairs)
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
     start.record(stream)
-    for e0, e1, e2 in ev:
-        e0.record(stream)
+    for i in range(args.steps):
+        mark(step_ev[3 * i])
         fwd()
-        e1.record(stream)
+        mark(step_ev[3 * i + 1])
         bwd()
-        e2.record(stream)
+        mark(step_ev[3 * i + 2])
     stop.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall
@@ -281,17 +300,13 @@ def main() -> int:
     if recorded >= n_pairs:
         raise RuntimeError("more contraction launches than timing events: the per-step "
                            "kernel time would be incomplete")
-    kern_ms = []
-    for i in range(recorded):
-        ms_i = ctypes.c_float(0.0)
-        _hip_ok(hip.hipEventElapsedTime(ctypes.byref(ms_i), ctypes.c_void_p(evs[2 * i]),
-                                        ctypes.c_void_p(evs[2 * i + 1])))
-        kern_ms.append(ms_i.value)
-    for i in range(2 * n_pairs):
+    kern_ms = [elapsed(evs[2 * i], evs[2 * i + 1]) for i in range(recorded)]
+    fwd_ms = sum(elapsed(step_ev[3 * i], step_ev[3 * i + 1]) for i in range(args.steps)) / args.steps
+    bwd_ms = sum(elapsed(step_ev[3 * i + 1], step_ev[3 * i + 2])
+                 for i in range(args.steps)) / args.steps
+    for i in range(2 * n_pairs + n_step_ev):
         hip.hipEventDestroy(ctypes.c_void_p(evs[i]))
     total_ms = start.elapsed_time(stop)
-    fwd_ms = sum(e0.elapsed_time(e1) for e0, e1, _ in ev) / args.steps
-    bwd_ms = sum(e1.elapsed_time(e2) for _, e1, e2 in ev) / args.steps
     ms = total_ms / args.steps
     flops = 8.0 * n * hd * v
     tflops = flops / (ms * 1e-3) / 1e12

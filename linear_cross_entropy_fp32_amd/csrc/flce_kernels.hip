@@ -547,14 +547,22 @@ bwd_dz_kernel(const DzArgs a) {
 // Workgroups [0, gh_wgs): grad_hidden (+)= dz[:, chunk] . W[chunk, :], split
 // over the chunk's vocabulary into gh_splits partial slots.  The rest:
 // grad_weight[chunk, :] = dz[:, chunk]^T . h.
+
+// cache-policy operand of a buffer store: the non-temporal (nt) bit
+constexpr int kStoreNonTemporal = 2;
+
 template <class T>
 __device__ __forceinline__ void store_tile(const T& tile, float* c, int64_t ldc, int m0, int n0,
-                                           int m_bound, int n_bound, bool accumulate) {
+                                           int m_bound, int n_bound, bool accumulate,
+                                           bool stream = false) {
   // Rows past m_bound fall outside the descriptor (based at row m0; a tile's
   // rows stay within 2^31 bytes of it) and read zero / are dropped; columns
   // past n_bound are sent out of range per lane.  No per-element branch, and
   // the 16 old values of a 32 x 32 block are loaded together, so an
-  // accumulating store costs one memory round trip per block.
+  // accumulating store costs one memory round trip per block.  `stream`
+  // marks results that nothing here reads again (grad_weight rows): their
+  // stores carry the non-temporal hint, which leaves fewer dirty L2 lines to
+  // write back when the kernel ends.
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave & 1, wn = wave >> 1;
   const __amdgpu_buffer_rsrc_t rs =
@@ -582,8 +590,13 @@ __device__ __forceinline__ void store_tile(const T& tile, float* c, int64_t ldc,
         for (int r = 0; r < 16; ++r) v[r] += old[r];
       }
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v[r]), rs, off[r], 0, 0);
+      for (int r = 0; r < 16; ++r) {
+        if (stream)
+          __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v[r]), rs, off[r], 0,
+                                                kStoreNonTemporal);
+        else
+          __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v[r]), rs, off[r], 0, 0);
+      }
     }
 }
 
@@ -624,7 +637,7 @@ contract_kernel(const ContractArgs a) {
     GwTile T;
     T.zero();
     T.run(lds, opA, opB, opB, false, 0, a.n);
-    store_tile(T, a.gw, a.hdim, tm * kGemmTileM, tn * kGemmTileN, a.width, a.hdim, false);
+    store_tile(T, a.gw, a.hdim, tm * kGemmTileM, tn * kGemmTileN, a.width, a.hdim, false, true);
   }
 }
 
