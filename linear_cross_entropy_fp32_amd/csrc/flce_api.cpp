@@ -101,7 +101,7 @@ Plan make_plan(const flce_problem* p) {
   splits = std::max<int64_t>(1, std::min<int64_t>(splits, pl.n_voc_tiles));
   pl.tiles_per_split = (int)cdiv(pl.n_voc_tiles, splits);
   pl.n_splits = (int)cdiv(pl.n_voc_tiles, pl.tiles_per_split);
-  pl.fin_blocks = (int)cdiv(n, 32);
+  pl.fin_blocks = (int)cdiv(n, kFinalTokens);
   const int64_t hidden_bf16_bytes = n * h * 2 * (p->hidden_dtype == FLCE_F32 ? 2 : 1);
   pl.tt_fastest = hidden_bf16_bytes <= kL2Bytes ? 1 : 0;
 

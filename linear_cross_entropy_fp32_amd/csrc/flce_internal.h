@@ -15,6 +15,7 @@ constexpr int kLogitTileN = 32768 / FLCE_LOGIT_TILE_V;
 constexpr int kGemmTileM = 256;
 constexpr int kGemmTileN = 128;
 constexpr int kSliceK = 32;   // K values per pipeline slice
+constexpr int kFinalTokens = 8;   // tokens per block of the forward merge
 
 // Online softmax state of one token over a range of vocabulary rows, in base-2
 // units (u = z * log2 e): running max m, S = sum 2^(u-m), T = sum 2^(u-m) u,

@@ -312,21 +312,30 @@ fwd_stats_kernel(const FwdArgs a) {
 }
 
 // ------------------------------------------------------- forward: K2 merge
-// 8 threads per token merge interleaved subsets of the splits, then a fixed
-// xor tree merges the 8 partial states; the first thread of each token
-// derives lse, loss, entropy, argmax and hit.  Each block writes fixed-order
-// partial sums for the reductions.
-constexpr int kMergeLanes = 8;
-constexpr int kFinalTokens = 256 / kMergeLanes;
+// 32 threads (half a wave) per token merge interleaved subsets of the splits
+// (split sub, sub + 32, ...), then a fixed xor tree merges the 32 partial
+// states; the first thread of each token derives lse, loss, entropy, argmax
+// and hit.  Each block writes fixed-order partial sums for the reductions.
+constexpr int kMergeLanes = 256 / kFinalTokens;
+static_assert(kMergeLanes == 32, "a token's merge lanes are one half-wave");
 
 __global__ void __launch_bounds__(256)
 fwd_finalize_kernel(const FinalArgs a) {
   const int sub = threadIdx.x % kMergeLanes;
   const int n = blockIdx.x * kFinalTokens + threadIdx.x / kMergeLanes;
   PartState st{kNegInf, 0.f, 0.f, kNegInf, kNegInf, 0x7fffffff};
-  if (n < a.n)
-    for (int s = sub; s < a.n_splits; s += kMergeLanes)
-      st = merge_state(st, a.part[(int64_t)s * a.n + n]);
+  if (n < a.n) {
+    int s = sub;
+    // four loads in flight before they are merged, in split order
+    for (; s + 3 * kMergeLanes < a.n_splits; s += 4 * kMergeLanes) {
+      PartState q[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) q[i] = a.part[(int64_t)(s + i * kMergeLanes) * a.n + n];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) st = merge_state(st, q[i]);
+    }
+    for (; s < a.n_splits; s += kMergeLanes) st = merge_state(st, a.part[(int64_t)s * a.n + n]);
+  }
 #pragma unroll
   for (int m = 1; m < kMergeLanes; m <<= 1) st = merge_state(st, shfl_xor_state(st, m));
 
@@ -355,15 +364,56 @@ fwd_finalize_kernel(const FinalArgs a) {
     nc = hit;
     nb = (!ignored && !valid);
   }
-  __shared__ double sl[256], se[256];
-  __shared__ int sv[256], sc[256], sb[256];
-  sl[threadIdx.x] = l_sum;
-  se[threadIdx.x] = e_sum;
+  // the block's tokens in order (one value per token, from its first lane)
+  __shared__ double sl[kFinalTokens], se[kFinalTokens];
+  __shared__ int sv[kFinalTokens], sc[kFinalTokens], sb[kFinalTokens];
+  if (sub == 0) {
+    const int k = threadIdx.x / kMergeLanes;
+    sl[k] = l_sum;
+    se[k] = e_sum;
+    sv[k] = nv;
+    sc[k] = nc;
+    sb[k] = nb;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    BlockSums r{0.0, 0.0, 0, 0, 0, 0};
+    for (int k = 0; k < kFinalTokens; ++k) {
+      r.loss += sl[k];
+      r.entropy += se[k];
+      r.n_valid += sv[k];
+      r.n_correct += sc[k];
+      r.n_bad += sb[k];
+    }
+    a.block_sums[blockIdx.x] = r;
+  }
+}
+
+// The block sums in a fixed order: thread i adds blocks i, i + 256, ... in
+// sequence, then a fixed tree adds the 256 thread sums.
+constexpr int kReduceThreads = 256;
+
+__global__ void __launch_bounds__(kReduceThreads)
+fwd_reduce_kernel(const BlockSums* __restrict__ bs, int nblocks, float mean_divisor,
+                  float* __restrict__ red_f32, int64_t* __restrict__ red_i64) {
+  double l = 0.0, e = 0.0;
+  int64_t nv = 0, nc = 0, nb = 0;
+  for (int i = threadIdx.x; i < nblocks; i += kReduceThreads) {
+    l += bs[i].loss;
+    e += bs[i].entropy;
+    nv += bs[i].n_valid;
+    nc += bs[i].n_correct;
+    nb += bs[i].n_bad;
+  }
+  __shared__ double sl[kReduceThreads], se[kReduceThreads];
+  __shared__ int64_t sv[kReduceThreads], sc[kReduceThreads], sb[kReduceThreads];
+  sl[threadIdx.x] = l;
+  se[threadIdx.x] = e;
   sv[threadIdx.x] = nv;
   sc[threadIdx.x] = nc;
   sb[threadIdx.x] = nb;
   __syncthreads();
-  for (int w = 128; w > 0; w >>= 1) {
+  for (int w = kReduceThreads / 2; w > 0; w >>= 1) {
     if (threadIdx.x < w) {
       sl[threadIdx.x] += sl[threadIdx.x + w];
       se[threadIdx.x] += se[threadIdx.x + w];
@@ -373,22 +423,12 @@ fwd_finalize_kernel(const FinalArgs a) {
     }
     __syncthreads();
   }
-  if (threadIdx.x == 0) a.block_sums[blockIdx.x] = BlockSums{sl[0], se[0], sv[0], sc[0], sb[0], 0};
-}
-
-__global__ void fwd_reduce_kernel(const BlockSums* __restrict__ bs, int nblocks,
-                                  float mean_divisor, float* __restrict__ red_f32,
-                                  int64_t* __restrict__ red_i64) {
-  if (threadIdx.x != 0 || blockIdx.x != 0) return;
-  double l = 0.0, e = 0.0;
-  int64_t nv = 0, nc = 0, nb = 0;
-  for (int i = 0; i < nblocks; ++i) {
-    l += bs[i].loss;
-    e += bs[i].entropy;
-    nv += bs[i].n_valid;
-    nc += bs[i].n_correct;
-    nb += bs[i].n_bad;
-  }
+  if (threadIdx.x != 0) return;
+  l = sl[0];
+  e = se[0];
+  nv = sv[0];
+  nc = sc[0];
+  nb = sb[0];
   const double div = mean_divisor > 0.f ? (double)mean_divisor : (double)nv;
   red_f32[0] = (float)l;
   red_f32[1] = div > 0.0 ? (float)(l / div) : 0.f;
@@ -733,7 +773,8 @@ hipError_t launch_fwd_stats(const FwdArgs& a, bool cap, bool fixed_ref, hipStrea
 hipError_t launch_fwd_finalize(const FinalArgs& a, int nblocks, float mean_divisor,
                                float* red_f32, int64_t* red_i64, hipStream_t s) {
   if (nblocks > 0) fwd_finalize_kernel<<<nblocks, 256, 0, s>>>(a);
-  fwd_reduce_kernel<<<1, 64, 0, s>>>(a.block_sums, nblocks, mean_divisor, red_f32, red_i64);
+  fwd_reduce_kernel<<<1, kReduceThreads, 0, s>>>(a.block_sums, nblocks, mean_divisor, red_f32,
+                                                  red_i64);
   return hipGetLastError();
 }
 
