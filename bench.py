@@ -16,6 +16,8 @@ import os
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
@@ -28,7 +30,10 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--cold-steps", type=int, default=10,
+                    help="after the timed steps, this many steps each preceded (outside their "
+                         "event bracket) by a 512 MiB write that evicts L2 and MALL; 0 = none")
     ap.add_argument("--workload", default="huge_vocab")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -301,6 +306,7 @@ def main() -> int:
         raise RuntimeError("more contraction launches than timing events: the per-step "
                            "kernel time would be incomplete")
     kern_ms = [elapsed(evs[2 * i], evs[2 * i + 1]) for i in range(recorded)]
+    step_ms = [elapsed(step_ev[3 * i], step_ev[3 * i + 2]) for i in range(args.steps)]
     fwd_ms = sum(elapsed(step_ev[3 * i], step_ev[3 * i + 1]) for i in range(args.steps)) / args.steps
     bwd_ms = sum(elapsed(step_ev[3 * i + 1], step_ev[3 * i + 2])
                  for i in range(args.steps)) / args.steps
@@ -308,6 +314,27 @@ def main() -> int:
         hip.hipEventDestroy(ctypes.c_void_p(evs[i]))
     total_ms = start.elapsed_time(stop)
     ms = total_ms / args.steps
+
+    # cold steps: every step starts with L2 and MALL (256 MB) holding none of
+    # its operands, after a 512 MiB write outside the step's event bracket
+    cold_ms = []
+    if args.cold_steps > 0:
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        cev = (ctypes.c_void_p * (2 * args.cold_steps))()
+        for i in range(2 * args.cold_steps):
+            _hip_ok(hip.hipEventCreateWithFlags(
+                ctypes.byref(cev, i * ctypes.sizeof(ctypes.c_void_p)), _EVENT_TIMING_ONLY))
+        for i in range(args.cold_steps):
+            flush.fill_(i & 255)
+            mark(cev[2 * i])
+            fwd()
+            bwd()
+            mark(cev[2 * i + 1])
+        torch.cuda.synchronize()
+        cold_ms = [elapsed(cev[2 * i], cev[2 * i + 1]) for i in range(args.cold_steps)]
+        for i in range(2 * args.cold_steps):
+            hip.hipEventDestroy(ctypes.c_void_p(cev[i]))
+        del flush
     flops = 8.0 * n * hd * v
     tflops = flops / (ms * 1e-3) / 1e12
     # dominant kernel: the backward contraction (grad_hidden and grad_weight of
@@ -328,6 +355,9 @@ def main() -> int:
                    "softcap": w.softcap, "reduction": w.reduction},
         "tflops": tflops, "pct_bf16_peak": 100.0 * tflops / PEAK_BF16_TFLOPS,
         "fwd_ms": fwd_ms, "bwd_ms": bwd_ms, "wall_s": wall,
+        "step_ms_p20_p50_p80": [float(np.percentile(step_ms, q)) for q in (20, 50, 80)],
+        "cold_step_ms_p20_p50_p80": ([float(np.percentile(cold_ms, q)) for q in (20, 50, 80)]
+                                     if cold_ms else None),
         "roofline": {"bound": "mfma", "kernel": "contract_kernel", "achieved": kern_tflops,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": kern_tflops / PEAK_BF16_TFLOPS, "traffic": traffic,
