@@ -14,9 +14,10 @@
  *   argmax[n]   = lowest v with z[n, v] = max_v z[n, v];  hit[n] = (argmax == t_n)
  *
  * without ever storing the (tokens x vocab) logits, plus the backward
- * grad_hidden / grad_weight / grad_bias.  Rows whose target equals
- * ignore_index are still projected (the review's "Correctness" item 2) but
- * carry no loss and no gradient.
+ * grad_hidden / grad_weight / grad_bias.  By default, rows whose target
+ * equals ignore_index are still projected but carry no loss and no gradient,
+ * as the review's "Correctness" item 2 describes.  With compact_valid set,
+ * they are left out of the work instead: see flce_problem.
  *
  * Conventions for every entry point:
  *   - all tensor pointers are DEVICE pointers, row-major and contiguous;
@@ -68,7 +69,16 @@ typedef struct flce_problem {
   int64_t ignore_index;  /* usually -100                                          */
   float mean_divisor;    /* > 0: the mean divides by it (num_items_in_batch);
                             otherwise by n_valid.  0 valid rows -> mean 0.        */
-  int32_t reserved;      /* must be 0                                             */
+  int32_t compact_valid; /* 0 or 1.  1 = valid-row compaction: the rows that carry
+                            a loss (target in [0, V), not ignore_index) are
+                            gathered on the device and only they are projected,
+                            forward and backward, with no host sync, so the work
+                            scales with n_valid instead of N.  The other rows get
+                            loss = entropy = 0, hit = 0, lse = 0, argmax = -1
+                            and grad_hidden = 0 (without compaction lse and
+                            argmax are computed for every row).  The valid rows'
+                            results and the gradients are the same in both
+                            modes up to summation order.                        */
 } flce_problem;
 
 /* Check the problem description only (no HIP call).  0 or FLCE_ERR_*. */

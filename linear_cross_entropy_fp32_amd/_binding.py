@@ -32,7 +32,7 @@ class FlceProblem(ctypes.Structure):
                 ("vocab", ctypes.c_int64), ("hidden_dtype", ctypes.c_int32),
                 ("weight_dtype", ctypes.c_int32), ("logit_scale", ctypes.c_float),
                 ("softcap", ctypes.c_float), ("ignore_index", ctypes.c_int64),
-                ("mean_divisor", ctypes.c_float), ("reserved", ctypes.c_int32)]
+                ("mean_divisor", ctypes.c_float), ("compact_valid", ctypes.c_int32)]
 
 
 class FlceError(RuntimeError):
@@ -83,9 +83,11 @@ def _check(rc: int) -> None:
 
 def make_problem(n_tokens: int, hidden: int, vocab: int, hidden_dtype: int = FLCE_BF16,
                  weight_dtype: int = FLCE_BF16, logit_scale: float = 1.0, softcap: float = 0.0,
-                 ignore_index: int = -100, mean_divisor: float = 0.0) -> FlceProblem:
+                 ignore_index: int = -100, mean_divisor: float = 0.0,
+                 compact_valid: bool = False) -> FlceProblem:
     return FlceProblem(n_tokens, hidden, vocab, hidden_dtype, weight_dtype, logit_scale,
-                       softcap if softcap else 0.0, ignore_index, mean_divisor, 0)
+                       softcap if softcap else 0.0, ignore_index, mean_divisor,
+                       1 if compact_valid else 0)
 
 
 def flce_validate(prob: FlceProblem) -> int:
@@ -129,13 +131,13 @@ def _dtype_code(t: torch.Tensor) -> int:
 
 def problem_for(hidden: torch.Tensor, weight: torch.Tensor, logit_scale: float = 1.0,
                 softcap: Optional[float] = None, ignore_index: int = -100,
-                mean_divisor: float = 0.0) -> FlceProblem:
+                mean_divisor: float = 0.0, compact_valid: bool = False) -> FlceProblem:
     if hidden.dim() != 2 or weight.dim() != 2 or hidden.shape[1] != weight.shape[1]:
         raise ValueError(f"hidden {tuple(hidden.shape)} and weight {tuple(weight.shape)} "
                          "must be [N, H] and [V, H]")
     return make_problem(hidden.shape[0], hidden.shape[1], weight.shape[0], _dtype_code(hidden),
                         _dtype_code(weight), float(logit_scale), float(softcap or 0.0),
-                        int(ignore_index), float(mean_divisor))
+                        int(ignore_index), float(mean_divisor), compact_valid)
 
 
 def _require(t: torch.Tensor, name: str, device: torch.device) -> None:
@@ -149,11 +151,13 @@ def flce_forward(hidden: torch.Tensor, weight: torch.Tensor, targets: torch.Tens
                  bias: Optional[torch.Tensor] = None, logit_scale: float = 1.0,
                  softcap: Optional[float] = None, ignore_index: int = -100,
                  mean_divisor: float = 0.0, want_argmax: bool = True,
-                 workspace: Optional[torch.Tensor] = None) -> dict:
+                 workspace: Optional[torch.Tensor] = None,
+                 compact_valid: bool = False) -> dict:
     """Run ``flce_forward`` on the current stream.  Returns device tensors:
     loss, lse, entropy [N] f32, hit [N] u8, argmax [N] i32 (or None),
     reduced_f32 [3] (loss_sum, loss_mean, entropy_sum) and reduced_i64 [3]
-    (n_valid, n_correct, n_bad_target)."""
+    (n_valid, n_correct, n_bad_target).  compact_valid: project only the rows
+    that carry a loss (the others get lse 0 and argmax -1)."""
     if targets is None:
         raise ValueError("targets are required")
     dev = weight.device
@@ -165,7 +169,8 @@ def flce_forward(hidden: torch.Tensor, weight: torch.Tensor, targets: torch.Tens
         _require(bias, "bias", dev)
         if bias.dtype != torch.float32 or bias.shape != (weight.shape[0],):
             raise ValueError("bias must be float32 [V]")
-    prob = problem_for(hidden, weight, logit_scale, softcap, ignore_index, mean_divisor)
+    prob = problem_for(hidden, weight, logit_scale, softcap, ignore_index, mean_divisor,
+                       compact_valid)
     n = hidden.shape[0]
     ws_bytes = flce_workspace_bytes(prob)
     if workspace is None or workspace.numel() < ws_bytes:
@@ -191,7 +196,8 @@ def flce_backward(hidden: torch.Tensor, weight: torch.Tensor, targets: torch.Ten
                   logit_scale: float = 1.0, softcap: Optional[float] = None,
                   ignore_index: int = -100, mean_divisor: float = 0.0,
                   need_bias_grad: Optional[bool] = None,
-                  workspace: Optional[torch.Tensor] = None, out: Optional[dict] = None):
+                  workspace: Optional[torch.Tensor] = None, out: Optional[dict] = None,
+                  compact_valid: bool = False):
     """Run ``flce_backward`` on the current stream.  Returns fp32
     (grad_hidden [N, H], grad_weight [V, H], grad_bias [V] or None)."""
     dev = weight.device
@@ -205,7 +211,8 @@ def flce_backward(hidden: torch.Tensor, weight: torch.Tensor, targets: torch.Ten
         raise ValueError("per-token grad_out must have N elements")
     if grad_mode != FLCE_GRAD_PER_TOKEN and grad_out.numel() != 1:
         raise ValueError("mean/sum grad_out must have one element")
-    prob = problem_for(hidden, weight, logit_scale, softcap, ignore_index, mean_divisor)
+    prob = problem_for(hidden, weight, logit_scale, softcap, ignore_index, mean_divisor,
+                       compact_valid)
     ws_bytes = flce_workspace_bytes(prob)
     if workspace is None or workspace.numel() < ws_bytes:
         workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
@@ -230,12 +237,12 @@ _MODES = {"mean": FLCE_GRAD_MEAN, "sum": FLCE_GRAD_SUM, "none": FLCE_GRAD_PER_TO
 class _LinearCrossEntropy(torch.autograd.Function):
     @staticmethod
     def forward(ctx, hidden, weight, bias, targets, logit_scale, softcap, reduction,
-                num_items, ignore_index):
+                num_items, ignore_index, compact_valid):
         mean_div = float(num_items) if num_items else 0.0
         out = flce_forward(hidden, weight, targets, bias, logit_scale, softcap, ignore_index,
-                           mean_div, want_argmax=False)
+                           mean_div, want_argmax=False, compact_valid=compact_valid)
         ctx.save_for_backward(hidden, weight, bias, targets, out["lse"], out["reduced_i64"])
-        ctx.cfg = (logit_scale, softcap, reduction, mean_div, ignore_index)
+        ctx.cfg = (logit_scale, softcap, reduction, mean_div, ignore_index, compact_valid)
         if reduction == "none":
             loss = out["loss"]
         elif reduction == "sum":
@@ -248,29 +255,33 @@ class _LinearCrossEntropy(torch.autograd.Function):
     @staticmethod
     def backward(ctx, g_loss, _g_ent, _g_nc, _g_nv):
         hidden, weight, bias, targets, lse, red_i64 = ctx.saved_tensors
-        logit_scale, softcap, reduction, mean_div, ignore_index = ctx.cfg
+        logit_scale, softcap, reduction, mean_div, ignore_index, compact_valid = ctx.cfg
         g = g_loss.to(torch.float32).contiguous().reshape(-1)
         gh, gw, gb = flce_backward(hidden, weight, targets, lse, red_i64, _MODES[reduction], g,
                                    bias, logit_scale, softcap, ignore_index, mean_div,
-                                   need_bias_grad=bias is not None and ctx.needs_input_grad[2])
+                                   need_bias_grad=bias is not None and ctx.needs_input_grad[2],
+                                   compact_valid=compact_valid)
         gh = gh.to(hidden.dtype) if ctx.needs_input_grad[0] else None
         gw = gw.to(weight.dtype) if ctx.needs_input_grad[1] else None
-        return gh, gw, gb, None, None, None, None, None, None
+        return gh, gw, gb, None, None, None, None, None, None, None
 
 
 def linear_cross_entropy(hidden: torch.Tensor, weight: torch.Tensor, targets: torch.Tensor,
                          bias: Optional[torch.Tensor] = None, logit_scale: float = 1.0,
                          softcap: Optional[float] = None, reduction: str = "mean",
-                         num_items: Optional[float] = None, ignore_index: int = -100):
+                         num_items: Optional[float] = None, ignore_index: int = -100,
+                         compact_valid: bool = False):
     """Fused linear cross-entropy with autograd.
 
     Returns (loss, entropy_sum, n_correct, n_valid): loss is the mean / sum
     scalar or the per-token vector (reduction "none"), entropy_sum is fp32 and
     the two counts are int64 device scalars (no host synchronisation).
+    compact_valid: only the rows that carry a loss are projected (device-side
+    compaction), so the work scales with the number of valid rows.
     """
     if targets is None:
         raise ValueError("targets must be provided")
     if reduction not in _MODES:
         raise ValueError(f"reduction must be one of {sorted(_MODES)}")
     return _LinearCrossEntropy.apply(hidden, weight, bias, targets, logit_scale, softcap,
-                                     reduction, num_items, ignore_index)
+                                     reduction, num_items, ignore_index, bool(compact_valid))

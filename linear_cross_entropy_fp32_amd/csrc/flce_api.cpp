@@ -63,12 +63,16 @@ struct Plan {
   int tt_fastest;        // logit-tile workgroup order: token tile fastest when
                          // the bf16 hidden operand fits in one XCD's L2
   size_t off_hsplit, off_part, off_bsums, off_dz, off_ghpart, off_cspart;
+  // row compaction: perm [N] int32, cnt [2] int32, block scratch, compact
+  // bf16 hidden rows [N, H] (fp32 hidden: the hi / lo split rows instead)
+  size_t off_perm, off_cnt, off_blk, off_hc;
   size_t fwd_bytes, bwd_bytes, bytes;
 };
 
 int validate(const flce_problem* p) {
   if (!p) return fail(FLCE_ERR_NULL, "problem is NULL");
-  if (p->reserved != 0) return fail(FLCE_ERR_ARG, "problem.reserved must be 0");
+  if (p->compact_valid != 0 && p->compact_valid != 1)
+    return fail(FLCE_ERR_ARG, "problem.compact_valid must be 0 or 1");
   if (p->n_tokens < 0 || p->n_tokens > kMaxTokens)
     return fail(FLCE_ERR_SHAPE, "n_tokens=%lld out of range [0, 2^23)", (long long)p->n_tokens);
   if (p->vocab < 1 || p->vocab > kMaxRows)
@@ -129,6 +133,17 @@ Plan make_plan(const flce_problem* p) {
   size_t off = 0;
   pl.off_hsplit = off;
   if (p->hidden_dtype == FLCE_F32) off += aup(size_t(2) * n * h * 2);
+  pl.off_perm = pl.off_cnt = pl.off_blk = pl.off_hc = off;
+  if (p->compact_valid && n > 0) {
+    pl.off_perm = off;
+    off += aup(size_t(n) * 4);
+    pl.off_cnt = off;
+    off += aup(2 * 4);
+    pl.off_blk = off;
+    off += aup(size_t(2) * cdiv(n, 256) * 4);
+    pl.off_hc = off;
+    if (p->hidden_dtype == FLCE_BF16) off += aup(size_t(n) * h * 2);
+  }
   const size_t shared_end = off;
   pl.off_part = off;
   off += aup(size_t(pl.n_splits) * n * sizeof(PartState));
@@ -139,7 +154,9 @@ Plan make_plan(const flce_problem* p) {
   pl.off_dz = off;
   off += aup(size_t(n) * vc * 2);
   pl.off_ghpart = off;
-  if (pl.gh_splits > 1) off += aup(size_t(pl.gh_splits) * n * h * 4);
+  // the split-K slots; with the row compaction also for one split, since the
+  // final pass scatters the compact rows back
+  if (pl.gh_splits > 1 || p->compact_valid) off += aup(size_t(pl.gh_splits) * n * h * 4);
   pl.cs_segs = (int)std::max<int64_t>(1, std::min<int64_t>(cdiv(n, 256), kColsumElems / vc));
   pl.off_cspart = off;
   off += aup(size_t(pl.cs_segs) * vc * 4);
@@ -189,6 +206,64 @@ hipError_t timed(int kernel, hipStream_t s, F&& launch) {
 
 int hip_check(hipError_t e, const char* what) {
   if (e != hipSuccess) return fail(FLCE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return FLCE_OK;
+}
+
+// The hidden operand(s) of the kernels, and the row compaction when asked
+// for: perm, the device count of compact rows, and the device count of the
+// out-of-range targets it leaves out (all null without compaction).
+struct Rows {
+  const uint16_t* h0 = nullptr;
+  const uint16_t* h1 = nullptr;
+  const int* perm = nullptr;
+  const int* n_dev = nullptr;
+  const int* n_bad = nullptr;
+};
+
+int prepare_rows(const flce_problem* p, const Plan& pl, const void* hidden,
+                 const int64_t* targets, char* ws, hipStream_t s, Rows& r) {
+  const int64_t n = p->n_tokens, h = p->hidden;
+  int rc;
+  r = Rows{};
+  r.h0 = static_cast<const uint16_t*>(hidden);
+  if (n == 0) return FLCE_OK;
+  uint16_t* hi = reinterpret_cast<uint16_t*>(ws + pl.off_hsplit);
+  uint16_t* lo = hi + n * h;
+  if (p->compact_valid) {
+    int* perm = reinterpret_cast<int*>(ws + pl.off_perm);
+    int* cnt = reinterpret_cast<int*>(ws + pl.off_cnt);
+    int* blk = reinterpret_cast<int*>(ws + pl.off_blk);
+    if ((rc = hip_check(launch_compact(targets, (int)n, p->ignore_index, (int)p->vocab, blk, cnt,
+                                       perm, s),
+                        "compact")))
+      return rc;
+    r.perm = perm;
+    r.n_dev = cnt;
+    r.n_bad = cnt + 1;
+    if (p->hidden_dtype == FLCE_F32) {
+      if ((rc = hip_check(launch_gather_split(static_cast<const float*>(hidden), perm, cnt, n, h,
+                                              hi, lo, s),
+                          "gather_split")))
+        return rc;
+      r.h0 = hi;
+      r.h1 = lo;
+    } else {
+      uint16_t* hc = reinterpret_cast<uint16_t*>(ws + pl.off_hc);
+      if ((rc = hip_check(launch_gather_rows(static_cast<const uint16_t*>(hidden), perm, cnt, n,
+                                             h, hc, s),
+                          "gather_rows")))
+        return rc;
+      r.h0 = hc;
+    }
+    return FLCE_OK;
+  }
+  if (p->hidden_dtype == FLCE_F32) {
+    if ((rc = hip_check(launch_split_hidden(static_cast<const float*>(hidden), hi, lo, n * h, s),
+                        "split_hidden")))
+      return rc;
+    r.h0 = hi;
+    r.h1 = lo;
+  }
   return FLCE_OK;
 }
 
@@ -257,25 +332,18 @@ int flce_forward(const flce_problem* p, const void* hidden, const void* weight,
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
 
-  const uint16_t* h0 = static_cast<const uint16_t*>(hidden);
-  const uint16_t* h1 = nullptr;
-  if (p->hidden_dtype == FLCE_F32 && n > 0) {
-    uint16_t* hi = reinterpret_cast<uint16_t*>(ws + pl.off_hsplit);
-    uint16_t* lo = hi + n * p->hidden;
-    if ((rc = hip_check(launch_split_hidden(static_cast<const float*>(hidden), hi, lo,
-                                            n * p->hidden, s), "split_hidden")))
-      return rc;
-    h0 = hi;
-    h1 = lo;
-  }
+  Rows rows;
+  if ((rc = prepare_rows(p, pl, hidden, targets, ws, s, rows))) return rc;
   PartState* part = reinterpret_cast<PartState*>(ws + pl.off_part);
   if (n > 0) {
     FwdArgs a{};
     a.w = static_cast<const uint16_t*>(weight);
-    a.h0 = h0;
-    a.h1 = h1;
+    a.h0 = rows.h0;
+    a.h1 = rows.h1;
     a.bias = bias;
     a.tgt = targets;
+    a.perm = rows.perm;
+    a.n_dev = rows.n_dev;
     a.n = (int)n;
     a.hdim = (int)p->hidden;
     a.v = (int)p->vocab;
@@ -307,8 +375,10 @@ int flce_forward(const flce_problem* p, const void* hidden, const void* weight,
   f.hit = hit;
   f.argmax = argmax;
   f.block_sums = reinterpret_cast<BlockSums*>(ws + pl.off_bsums);
+  f.perm = rows.perm;
+  f.n_dev = rows.n_dev;
   return hip_check(launch_fwd_finalize(f, pl.fin_blocks, p->mean_divisor > 0 ? p->mean_divisor : 0.f,
-                                       reduced_f32, reduced_i64, s),
+                                       reduced_f32, reduced_i64, rows.n_bad, s),
                    "fwd_finalize");
 }
 
@@ -349,17 +419,11 @@ int flce_backward(const flce_problem* p, const void* hidden, const void* weight,
     return FLCE_OK;
   }
 
-  const uint16_t* h0 = static_cast<const uint16_t*>(hidden);
-  const uint16_t* h1 = nullptr;
-  if (p->hidden_dtype == FLCE_F32) {
-    uint16_t* hi = reinterpret_cast<uint16_t*>(ws + pl.off_hsplit);
-    uint16_t* lo = hi + n * h;
-    if ((rc = hip_check(launch_split_hidden(static_cast<const float*>(hidden), hi, lo, n * h, s),
-                        "split_hidden")))
-      return rc;
-    h0 = hi;
-    h1 = lo;
-  }
+  Rows rows;
+  if ((rc = prepare_rows(p, pl, hidden, targets, ws, s, rows))) return rc;
+  const uint16_t* h0 = rows.h0;
+  const uint16_t* h1 = rows.h1;
+  const bool slots = pl.gh_splits > 1 || rows.perm != nullptr;   // grad_hidden via the slots
   uint16_t* dz = reinterpret_cast<uint16_t*>(ws + pl.off_dz);
   float* ghpart = reinterpret_cast<float*>(ws + pl.off_ghpart);
 
@@ -385,6 +449,8 @@ int flce_backward(const flce_problem* p, const void* hidden, const void* weight,
   d.tiles_per_wg = pl.dz_tiles_per_wg;
   d.dz = dz;
   d.ldz = pl.vc;
+  d.perm = rows.perm;
+  d.n_dev = rows.n_dev;
 
   ContractArgs g{};
   g.dz = dz;
@@ -396,7 +462,8 @@ int flce_backward(const flce_problem* p, const void* hidden, const void* weight,
   g.gh_kps = (int)pl.gh_kps;
   g.gh_m_tiles = (int)cdiv(n, kGemmTileM);
   g.n_tiles = (int)cdiv(h, kGemmTileN);
-  g.gh = pl.gh_splits > 1 ? ghpart : grad_hidden;
+  g.gh = slots ? ghpart : grad_hidden;
+  g.n_dev = rows.n_dev;
 
   for (int c = 0; c < pl.n_chunks; ++c) {
     const int64_t c0 = int64_t(c) * pl.vc;
@@ -421,12 +488,13 @@ int flce_backward(const flce_problem* p, const void* hidden, const void* weight,
     if (grad_bias &&
         (rc = hip_check(launch_colsum(dz, pl.vc, (int)n, (int)width, pl.cs_segs,
                                       reinterpret_cast<float*>(ws + pl.off_cspart),
-                                      grad_bias + c0, s),
+                                      grad_bias + c0, rows.n_dev, s),
                         "colsum")))
       return rc;
   }
-  if (pl.gh_splits > 1 &&
-      (rc = hip_check(launch_sum_partials(ghpart, pl.gh_splits, n * h, grad_hidden, n * h, s),
+  if (slots &&
+      (rc = hip_check(launch_sum_partials(ghpart, pl.gh_splits, n * h, grad_hidden, n * h, h,
+                                          rows.perm, rows.n_dev, s),
                       "sum_partials")))
     return rc;
   return FLCE_OK;

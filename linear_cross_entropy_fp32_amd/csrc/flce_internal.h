@@ -41,6 +41,10 @@ struct FwdArgs {
   int n_tok_tiles, n_splits, tiles_per_split, n_voc_tiles;
   int tt_fastest;        // workgroup order (see grouped_order)
   PartState* part;       // [n_splits, N]
+  // row compaction (both null without it): compact row c is row perm[c] of
+  // tgt; only rows c < *n_dev are computed (the hidden rows are compacted)
+  const int* perm;
+  const int* n_dev;
 };
 
 struct FinalArgs {
@@ -54,6 +58,10 @@ struct FinalArgs {
   uint8_t* hit;
   int32_t* argmax;       // may be null
   BlockSums* block_sums;
+  // row compaction (both null without it): compact row c is row perm[c]; rows
+  // c >= *n_dev get zero outputs (lse 0, argmax -1)
+  const int* perm;
+  const int* n_dev;
 };
 
 struct DzArgs {
@@ -78,6 +86,10 @@ struct DzArgs {
   int tt_fastest;        // workgroup order (see grouped_order)
   uint16_t* dz;          // [N, ldz] bf16 chunk buffer
   int64_t ldz;
+  // row compaction (both null without it): dz row c belongs to row perm[c] of
+  // tgt, lse and grad_out; only rows c < *n_dev are computed
+  const int* perm;
+  const int* n_dev;
 };
 
 // One launch per vocab chunk computes both contractions of the chunk's dz:
@@ -93,20 +105,37 @@ struct ContractArgs {
   float* gh;             // [gh_splits, N, H] partials, or grad_hidden when gh_splits == 1
   int gh_accumulate;
   float* gw;             // grad_weight + c0 * H
+  const int* n_dev;      // row compaction: only dz rows c < *n_dev are used; else null
 };
 
 hipError_t launch_split_hidden(const float* h, uint16_t* hi, uint16_t* lo, int64_t count,
                                hipStream_t s);
 hipError_t launch_fwd_stats(const FwdArgs& a, bool cap, bool fixed_ref, hipStream_t s);
+// n_bad_extra: null, or a device count of out-of-range targets that the
+// finalize did not see (rows left out by the row compaction)
 hipError_t launch_fwd_finalize(const FinalArgs& a, int nblocks, float mean_divisor,
-                               float* red_f32, int64_t* red_i64, hipStream_t s);
+                               float* red_f32, int64_t* red_i64, const int* n_bad_extra,
+                               hipStream_t s);
 hipError_t launch_bwd_dz(const DzArgs& a, bool cap, hipStream_t s);
 hipError_t launch_contract(const ContractArgs& a, hipStream_t s);
+// out[perm[c], :] = sum_z part[z][c, :] for rows c < *n_dev and 0 for the
+// other rows (perm, n_dev null: out = sum_z part[z]); rows of hdim floats.
 hipError_t launch_sum_partials(const float* part, int nsplit, int64_t stride, float* out,
-                               int64_t count, hipStream_t s);
+                               int64_t count, int64_t hdim, const int* perm, const int* n_dev,
+                               hipStream_t s);
 // grad_bias of one chunk; part: nseg * width floats of workspace.
 hipError_t launch_colsum(const uint16_t* dz, int64_t ldz, int n_tok, int width, int nseg,
-                         float* part, float* out, hipStream_t s);
+                         float* part, float* out, const int* n_dev, hipStream_t s);
+// Row compaction (see compact_scatter_kernel): perm [N], cnt [2] = {rows that
+// carry a loss, out-of-range targets}; blk: 2 * cdiv(N, 256) ints of scratch.
+// Then the hidden rows of the first cnt[0] compact rows are gathered into
+// out_h (bf16 hidden), or split into out_hi / out_lo (fp32 hidden).
+hipError_t launch_compact(const int64_t* tgt, int n, int64_t ignore, int v, int* blk, int* cnt,
+                          int* perm, hipStream_t s);
+hipError_t launch_gather_rows(const uint16_t* h, const int* perm, const int* cnt, int64_t n,
+                              int64_t hdim, uint16_t* out, hipStream_t s);
+hipError_t launch_gather_split(const float* h, const int* perm, const int* cnt, int64_t n,
+                               int64_t hdim, uint16_t* hi, uint16_t* lo, hipStream_t s);
 hipError_t launch_fill_zero(float* p, int64_t count, hipStream_t s);
 
 }  // namespace flce

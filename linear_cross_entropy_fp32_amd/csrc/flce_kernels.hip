@@ -151,6 +151,152 @@ __global__ void split_hidden_kernel(const float* __restrict__ h, uint16_t* __res
   }
 }
 
+// ------------------------------------------------------------ row compaction
+// Optional (flce_problem.compact_valid): the rows that carry a loss (target in
+// [0, V), not ignore_index) are listed first in perm, in row order, followed
+// by the other rows in row order, so perm is a permutation of [0, N); the
+// number of the former goes to cnt[0] and the number of out-of-range targets
+// to cnt[1].  Every kernel then runs over compact row c with the original row
+// perm[c], only for c < cnt[0].  Three passes: per-block counts, one block
+// scans them, every block writes its rows' positions.
+constexpr int kCompactBlock = 256;
+constexpr int kScanThreads = 1024;
+
+__device__ __forceinline__ void row_kind(const int64_t* tgt, int i, int n, int64_t ignore, int v,
+                                         bool& valid, bool& bad) {
+  valid = bad = false;
+  if (i < n) {
+    const int64_t t = tgt[i];
+    const bool ig = (t == ignore);
+    valid = !ig && t >= 0 && t < v;
+    bad = !ig && !valid;
+  }
+}
+
+__global__ void __launch_bounds__(kCompactBlock)
+compact_count_kernel(const int64_t* __restrict__ tgt, int n, int64_t ignore, int v,
+                     int* __restrict__ blk_valid, int* __restrict__ blk_bad) {
+  bool valid, bad;
+  row_kind(tgt, blockIdx.x * kCompactBlock + threadIdx.x, n, ignore, v, valid, bad);
+  const uint64_t bv = __ballot(valid), bb = __ballot(bad);
+  __shared__ int sv[kCompactBlock / 64], sb[kCompactBlock / 64];
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    sv[w] = __popcll(bv);
+    sb[w] = __popcll(bb);
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int a = 0, b = 0;
+    for (int i = 0; i < kCompactBlock / 64; ++i) {
+      a += sv[i];
+      b += sb[i];
+    }
+    blk_valid[blockIdx.x] = a;
+    blk_bad[blockIdx.x] = b;
+  }
+}
+
+// One block: blk_valid becomes its exclusive prefix sum; cnt = {total valid,
+// total out-of-range}.  Thread i scans a contiguous run of blocks.
+__global__ void __launch_bounds__(kScanThreads)
+compact_scan_kernel(int* __restrict__ blk_valid, const int* __restrict__ blk_bad, int nblk,
+                    int* __restrict__ cnt) {
+  const int per = (nblk + kScanThreads - 1) / kScanThreads;
+  const int b0 = threadIdx.x * per, b1 = min(nblk, b0 + per);
+  int sum = 0, bad = 0;
+  for (int b = b0; b < b1; ++b) {
+    sum += blk_valid[b];
+    bad += blk_bad[b];
+  }
+  __shared__ int ss[kScanThreads], sb[kScanThreads];
+  ss[threadIdx.x] = sum;
+  sb[threadIdx.x] = bad;
+  __syncthreads();
+  // inclusive scan of the thread sums (Hillis-Steele); bad counts are summed
+  for (int d = 1; d < kScanThreads; d <<= 1) {
+    const int x = threadIdx.x >= d ? ss[threadIdx.x - d] : 0;
+    const int y = threadIdx.x >= d ? sb[threadIdx.x - d] : 0;
+    __syncthreads();
+    ss[threadIdx.x] += x;
+    sb[threadIdx.x] += y;
+    __syncthreads();
+  }
+  int run = ss[threadIdx.x] - sum;
+  for (int b = b0; b < b1; ++b) {
+    const int c = blk_valid[b];
+    blk_valid[b] = run;
+    run += c;
+  }
+  if (threadIdx.x == kScanThreads - 1) {
+    cnt[0] = ss[kScanThreads - 1];
+    cnt[1] = sb[kScanThreads - 1];
+  }
+}
+
+__global__ void __launch_bounds__(kCompactBlock)
+compact_scatter_kernel(const int64_t* __restrict__ tgt, int n, int64_t ignore, int v,
+                       const int* __restrict__ blk_off, const int* __restrict__ cnt,
+                       int* __restrict__ perm) {
+  const int i = blockIdx.x * kCompactBlock + threadIdx.x;
+  bool valid, bad;
+  row_kind(tgt, i, n, ignore, v, valid, bad);
+  const bool other = (i < n) && !valid;
+  const uint64_t bv = __ballot(valid), bo = __ballot(other);
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  __shared__ int sv[kCompactBlock / 64], so[kCompactBlock / 64];
+  if (lane == 0) {
+    sv[w] = __popcll(bv);
+    so[w] = __popcll(bo);
+  }
+  __syncthreads();
+  int rv = __popcll(bv & below), ro = __popcll(bo & below);
+  for (int k = 0; k < w; ++k) {
+    rv += sv[k];
+    ro += so[k];
+  }
+  if (i >= n) return;
+  const int vbefore = blk_off[blockIdx.x];                       // valid rows in earlier blocks
+  const int obefore = blockIdx.x * kCompactBlock - vbefore;      // other rows in earlier blocks
+  perm[valid ? vbefore + rv : cnt[0] + obefore + ro] = i;
+}
+
+// Compact hidden rows: out[c] = h[perm[c]] for c < cnt[0], 8 bf16 per thread.
+__global__ void gather_rows_kernel(const uint16_t* __restrict__ h, const int* __restrict__ perm,
+                                   const int* __restrict__ cnt, int64_t hdim,
+                                   uint16_t* __restrict__ out, int64_t n) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t per_row = hdim / 8;
+  const int64_t c = t / per_row, k = (t % per_row) * 8;
+  if (c >= n || c >= cnt[0]) return;
+  *reinterpret_cast<u32x4*>(out + c * hdim + k) =
+      *reinterpret_cast<const u32x4*>(h + (int64_t)perm[c] * hdim + k);
+}
+
+// fp32 hidden: gather and split in one pass, hi = bf16(h), lo = bf16(h - hi).
+__global__ void gather_split_kernel(const float* __restrict__ h, const int* __restrict__ perm,
+                                    const int* __restrict__ cnt, int64_t hdim,
+                                    uint16_t* __restrict__ hi, uint16_t* __restrict__ lo,
+                                    int64_t n) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t per_row = hdim / 8;
+  const int64_t c = t / per_row, k = (t % per_row) * 8;
+  if (c >= n || c >= cnt[0]) return;
+  const float* src = h + (int64_t)perm[c] * hdim + k;
+  u32x4 ph, pl;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float a = src[2 * i], b = src[2 * i + 1];
+    ph[i] = pack_bf16x2(a, b);
+    const float ah = __builtin_bit_cast(float, ph[i] << 16);
+    const float bh = __builtin_bit_cast(float, ph[i] & 0xffff0000u);
+    pl[i] = pack_bf16x2(a - ah, b - bh);
+  }
+  *reinterpret_cast<u32x4*>(hi + c * hdim + k) = ph;
+  *reinterpret_cast<u32x4*>(lo + c * hdim + k) = pl;
+}
+
 // ------------------------------------------------------------- forward: K1
 // Fold one token column (kQ values in a lane) of a finished logit tile into
 // that token's state.  `val` holds the values in place of the accumulators.
@@ -262,6 +408,8 @@ fwd_stats_kernel(const FwdArgs a) {
       grouped_order(xcd_remap(blockIdx.x, gridDim.x), a.n_tok_tiles, a.n_splits, a.tt_fastest);
   const int tt = gp.tt, sp = gp.grp;
   const int n0 = tt * kLogitTileN;
+  const int n_rows = a.n_dev ? *a.n_dev : a.n;   // rows computed (compacted rows first)
+  if (n0 >= n_rows) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave & 1, wn = wave >> 1;
   const int half = lane >> 5;
@@ -271,15 +419,15 @@ fwd_stats_kernel(const FwdArgs a) {
 #pragma unroll
   for (int j = 0; j < kColumns; ++j) {
     const int n = n0 + wn * (kLogitTileN / 2) + j * 32 + (lane & 31);
-    const int64_t t = (n < a.n) ? a.tgt[n] : -1;
+    const int64_t t = (n < n_rows) ? a.tgt[a.perm ? a.perm[n] : n] : -1;
     tgt[j] = (t >= 0 && t < a.v) ? (int)t : -(1 << 30);
     st[j] = PartState{FIXED ? 0.f : kNegInf, 0.f, 0.f, kNegInf, kNegInf, 0x7fffffff};
   }
   const int vt_begin = sp * a.tiles_per_split;
   const int ntiles = min(a.n_voc_tiles, vt_begin + a.tiles_per_split) - vt_begin;
   const Operand opA{a.w, a.hdim, vt_begin * kLogitTileV, a.v, a.hdim};
-  const Operand opB0{a.h0, a.hdim, n0, a.n, a.hdim};
-  const Operand opB1{a.h1 ? a.h1 : a.h0, a.hdim, n0, a.n, a.hdim};
+  const Operand opB0{a.h0, a.hdim, n0, n_rows, a.hdim};
+  const Operand opB1{a.h1 ? a.h1 : a.h0, a.hdim, n0, n_rows, a.hdim};
   FwdEpilogue<CAP, FIXED, BIAS> epi{a, st, tgt, vt_begin, wm, half};
   LogitTile T;
   T.run_stream(lds, opA, opB0, opB1, a.h1 != nullptr, a.hdim, ntiles, epi);
@@ -306,7 +454,7 @@ fwd_stats_kernel(const FwdArgs a) {
     for (int j = 0; j < kColumns; ++j) {
       const PartState o = merge_state(st[j], sh[(wn * kColumns + j) * 32 + lane]);
       const int n = n0 + wn * (kLogitTileN / 2) + j * 32 + lane;
-      if (n < a.n) a.part[(int64_t)sp * a.n + n] = o;
+      if (n < n_rows) a.part[(int64_t)sp * a.n + n] = o;
     }
   }
 }
@@ -322,9 +470,10 @@ static_assert(kMergeLanes == 32, "a token's merge lanes are one half-wave");
 __global__ void __launch_bounds__(256)
 fwd_finalize_kernel(const FinalArgs a) {
   const int sub = threadIdx.x % kMergeLanes;
-  const int n = blockIdx.x * kFinalTokens + threadIdx.x / kMergeLanes;
+  const int n = blockIdx.x * kFinalTokens + threadIdx.x / kMergeLanes;   // compact row
+  const int n_rows = a.n_dev ? *a.n_dev : a.n;
   PartState st{kNegInf, 0.f, 0.f, kNegInf, kNegInf, 0x7fffffff};
-  if (n < a.n) {
+  if (n < n_rows) {
     int s = sub;
     // four loads in flight before they are merged, in split order
     for (; s + 3 * kMergeLanes < a.n_splits; s += 4 * kMergeLanes) {
@@ -341,9 +490,18 @@ fwd_finalize_kernel(const FinalArgs a) {
 
   double l_sum = 0.0, e_sum = 0.0;
   int nv = 0, nc = 0, nb = 0;
-  if (n < a.n && sub == 0) {
+  if (n < a.n && sub == 0 && n >= n_rows) {
+    // a row left out by the row compaction: no loss, no statistics
+    const int row = a.perm[n];
+    a.loss[row] = 0.f;
+    a.lse[row] = 0.f;
+    a.entropy[row] = 0.f;
+    a.hit[row] = 0;
+    if (a.argmax) a.argmax[row] = -1;
+  } else if (n < a.n && sub == 0) {
+    const int row = a.perm ? a.perm[n] : n;
     const float lse2 = st.m + log2f(st.s);
-    const int64_t t = a.tgt[n];
+    const int64_t t = a.tgt[row];
     const bool ignored = (t == a.ignore_index);
     const bool valid = !ignored && t >= 0 && t < a.v;
     float loss = 0.f, ent = 0.f;
@@ -353,11 +511,11 @@ fwd_finalize_kernel(const FinalArgs a) {
       ent = (lse2 - st.t / st.s) * kLn2;
       hit = (st.bi == (int)t) ? 1 : 0;
     }
-    a.loss[n] = loss;
-    a.lse[n] = lse2 * kLn2;
-    a.entropy[n] = ent;
-    a.hit[n] = hit;
-    if (a.argmax) a.argmax[n] = st.bi;
+    a.loss[row] = loss;
+    a.lse[row] = lse2 * kLn2;
+    a.entropy[row] = ent;
+    a.hit[row] = hit;
+    if (a.argmax) a.argmax[row] = st.bi;
     l_sum = loss;
     e_sum = ent;
     nv = valid;
@@ -395,7 +553,8 @@ constexpr int kReduceThreads = 256;
 
 __global__ void __launch_bounds__(kReduceThreads)
 fwd_reduce_kernel(const BlockSums* __restrict__ bs, int nblocks, float mean_divisor,
-                  float* __restrict__ red_f32, int64_t* __restrict__ red_i64) {
+                  float* __restrict__ red_f32, int64_t* __restrict__ red_i64,
+                  const int* __restrict__ n_bad_extra) {
   double l = 0.0, e = 0.0;
   int64_t nv = 0, nc = 0, nb = 0;
   for (int i = threadIdx.x; i < nblocks; i += kReduceThreads) {
@@ -428,7 +587,7 @@ fwd_reduce_kernel(const BlockSums* __restrict__ bs, int nblocks, float mean_divi
   e = se[0];
   nv = sv[0];
   nc = sc[0];
-  nb = sb[0];
+  nb = sb[0] + (n_bad_extra ? *n_bad_extra : 0);
   const double div = mean_divisor > 0.f ? (double)mean_divisor : (double)nv;
   red_f32[0] = (float)l;
   red_f32[1] = div > 0.0 ? (float)(l / div) : 0.f;
@@ -558,6 +717,8 @@ bwd_dz_kernel(const DzArgs a) {
       grouped_order(xcd_remap(blockIdx.x, gridDim.x), a.n_tok_tiles, groups, a.tt_fastest);
   const int tt = gp.tt, grp = gp.grp;
   const int n0 = tt * kLogitTileN;
+  const int n_rows = a.n_dev ? *a.n_dev : a.n;   // rows computed (compacted rows first)
+  if (n0 >= n_rows) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave & 1, wn = wave >> 1;
   const int half = lane >> 5;
@@ -567,16 +728,18 @@ bwd_dz_kernel(const DzArgs a) {
 #pragma unroll
   for (int j = 0; j < kColumns; ++j) {
     const int n = n0 + wn * (kLogitTileN / 2) + j * 32 + (lane & 31);
-    const int64_t t = (n < a.n) ? a.tgt[n] : -1;
-    gs[j] = row_grad(a, n, t) * (CAP ? 4.0f : 1.0f);
-    nl[j] = (n < a.n) ? -a.lse[n] * kLog2e : 0.f;
+    const bool in = n < n_rows;
+    const int row = in ? (a.perm ? a.perm[n] : n) : 0;
+    const int64_t t = in ? a.tgt[row] : -1;
+    gs[j] = in ? row_grad(a, row, t) * (CAP ? 4.0f : 1.0f) : 0.f;
+    nl[j] = in ? -a.lse[row] * kLog2e : 0.f;
     tgt[j] = (t >= 0 && t < a.v) ? (int)t : -(1 << 30);
   }
   const int vt_begin = grp * a.tiles_per_wg;
   const int ntiles = min(a.chunk_tiles, vt_begin + a.tiles_per_wg) - vt_begin;
   const Operand opA{a.w, a.hdim, a.c0 + vt_begin * kLogitTileV, a.v, a.hdim};
-  const Operand opB0{a.h0, a.hdim, n0, a.n, a.hdim};
-  const Operand opB1{a.h1 ? a.h1 : a.h0, a.hdim, n0, a.n, a.hdim};
+  const Operand opB0{a.h0, a.hdim, n0, n_rows, a.hdim};
+  const Operand opB1{a.h1 ? a.h1 : a.h0, a.hdim, n0, n_rows, a.hdim};
   DzEpilogue<CAP, BIAS> epi{a, gs, nl, tgt, vt_begin, wm, half,
                            __builtin_amdgcn_readfirstlane(n0 + wn * (kLogitTileN / 2))};
   LogitTile T;
@@ -656,39 +819,52 @@ contract_kernel(const ContractArgs a) {
   const int gh_per_unit = a.gh_m_tiles * a.n_tiles;
   const int unit_size = gh_per_unit + a.gw_rows_per_unit * a.n_tiles;
   const int unit = bid / unit_size, off = bid % unit_size;
+  const int n_rows = a.n_dev ? *a.n_dev : a.n;   // dz rows in use (compacted rows first)
   if (off < gh_per_unit) {
     const int z = unit, rem = off;
     const int tm = rem / a.n_tiles, tn = rem % a.n_tiles;
+    if (tm * kGemmTileM >= n_rows) return;
     const int kb = z * a.gh_kps;
     const int ke = min(a.width, kb + a.gh_kps);
-    const Operand opA{a.dz, a.ldz, tm * kGemmTileM, a.n, width8};
+    const Operand opA{a.dz, a.ldz, tm * kGemmTileM, n_rows, width8};
     const Operand opB{a.w, a.hdim, tn * kGemmTileN, a.hdim, a.width};
     GhTile T;
     T.zero();
     T.run(lds, opA, opB, opB, false, kb, ke);
     store_tile(T, a.gh + (int64_t)z * a.n * a.hdim, a.hdim, tm * kGemmTileM, tn * kGemmTileN,
-               a.n, a.hdim, a.gh_accumulate != 0);
+               n_rows, a.hdim, a.gh_accumulate != 0);
   } else {
     const int b = off - gh_per_unit;
     const int tm = unit * a.gw_rows_per_unit + b / a.n_tiles, tn = b % a.n_tiles;
     if (tm >= a.gw_m_tiles) return;
-    const Operand opA{a.dz, a.ldz, tm * kGemmTileM, width8, a.n};
-    const Operand opB{a.h, a.hdim, tn * kGemmTileN, a.hdim, a.n};
+    const Operand opA{a.dz, a.ldz, tm * kGemmTileM, width8, n_rows};
+    const Operand opB{a.h, a.hdim, tn * kGemmTileN, a.hdim, n_rows};
     GwTile T;
     T.zero();
-    T.run(lds, opA, opB, opB, false, 0, a.n);
+    T.run(lds, opA, opB, opB, false, 0, n_rows);
     store_tile(T, a.gw, a.hdim, tm * kGemmTileM, tn * kGemmTileN, a.width, a.hdim, false, true);
   }
 }
 
-// out[i] = sum_z part[z][i], z in order.
+// out[i] = sum_z part[z][i], z in order.  With the row compaction, element i
+// of compact row c goes to row perm[c], and rows c >= *n_dev are zero.
 __global__ void sum_partials_kernel(const float* __restrict__ part, int nsplit, int64_t stride,
-                                    float* __restrict__ out, int64_t count) {
+                                    float* __restrict__ out, int64_t count, int64_t hdim,
+                                    const int* __restrict__ perm, const int* __restrict__ n_dev) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= count) return;
+  int64_t o = i;
+  if (perm) {
+    const int64_t c = i / hdim;
+    o = (int64_t)perm[c] * hdim + (i - c * hdim);
+    if (c >= *n_dev) {
+      out[o] = 0.f;
+      return;
+    }
+  }
   float s = part[i];
   for (int z = 1; z < nsplit; ++z) s += part[(int64_t)z * stride + i];
-  out[i] = s;
+  out[o] = s;
 }
 
 // grad_bias of one chunk, gb[v] = sum_n dz[n, v] (fp32 accumulation of the bf16
@@ -700,7 +876,8 @@ __global__ void sum_partials_kernel(const float* __restrict__ part, int nsplit, 
 constexpr int kColBlock = 512;
 __global__ void __launch_bounds__(256)
 colsum_partial_kernel(const uint16_t* __restrict__ dz, int64_t ldz, int n_tok, int width,
-                      int rows_per_seg, float* __restrict__ part) {
+                      int rows_per_seg, float* __restrict__ part, const int* __restrict__ n_dev) {
+  if (n_dev) n_tok = min(n_tok, *n_dev);
   const int cg = threadIdx.x & 63, ph = threadIdx.x >> 6;
   const int c0 = blockIdx.x * kColBlock + cg * 8;
   const int seg = blockIdx.y;
@@ -771,10 +948,11 @@ hipError_t launch_fwd_stats(const FwdArgs& a, bool cap, bool fixed_ref, hipStrea
 }
 
 hipError_t launch_fwd_finalize(const FinalArgs& a, int nblocks, float mean_divisor,
-                               float* red_f32, int64_t* red_i64, hipStream_t s) {
+                               float* red_f32, int64_t* red_i64, const int* n_bad_extra,
+                               hipStream_t s) {
   if (nblocks > 0) fwd_finalize_kernel<<<nblocks, 256, 0, s>>>(a);
   fwd_reduce_kernel<<<1, kReduceThreads, 0, s>>>(a.block_sums, nblocks, mean_divisor, red_f32,
-                                                  red_i64);
+                                                  red_i64, n_bad_extra);
   return hipGetLastError();
 }
 
@@ -802,21 +980,49 @@ hipError_t launch_contract(const ContractArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_sum_partials(const float* part, int nsplit, int64_t stride, float* out,
-                               int64_t count, hipStream_t s) {
+                               int64_t count, int64_t hdim, const int* perm, const int* n_dev,
+                               hipStream_t s) {
   if (count == 0) return hipSuccess;
-  sum_partials_kernel<<<grid1(count, 256), 256, 0, s>>>(part, nsplit, stride, out, count);
+  sum_partials_kernel<<<grid1(count, 256), 256, 0, s>>>(part, nsplit, stride, out, count, hdim,
+                                                        perm, n_dev);
   return hipGetLastError();
 }
 
 hipError_t launch_colsum(const uint16_t* dz, int64_t ldz, int n_tok, int width, int nseg,
-                         float* part, float* out, hipStream_t s) {
+                         float* part, float* out, const int* n_dev, hipStream_t s) {
   if (width == 0) return hipSuccess;
   if (n_tok == 0) return launch_fill_zero(out, width, s);
   const int rows_per_seg = (n_tok + nseg - 1) / nseg;
   nseg = (n_tok + rows_per_seg - 1) / rows_per_seg;
   const dim3 grid((unsigned)((width + kColBlock - 1) / kColBlock), (unsigned)nseg);
-  colsum_partial_kernel<<<grid, 256, 0, s>>>(dz, ldz, n_tok, width, rows_per_seg, part);
+  colsum_partial_kernel<<<grid, 256, 0, s>>>(dz, ldz, n_tok, width, rows_per_seg, part, n_dev);
   colsum_reduce_kernel<<<grid1(width, 256), 256, 0, s>>>(part, nseg, width, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_compact(const int64_t* tgt, int n, int64_t ignore, int v, int* blk, int* cnt,
+                          int* perm, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  const int nblk = (n + kCompactBlock - 1) / kCompactBlock;
+  compact_count_kernel<<<nblk, kCompactBlock, 0, s>>>(tgt, n, ignore, v, blk, blk + nblk);
+  compact_scan_kernel<<<1, kScanThreads, 0, s>>>(blk, blk + nblk, nblk, cnt);
+  compact_scatter_kernel<<<nblk, kCompactBlock, 0, s>>>(tgt, n, ignore, v, blk, cnt, perm);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_rows(const uint16_t* h, const int* perm, const int* cnt, int64_t n,
+                              int64_t hdim, uint16_t* out, hipStream_t s) {
+  const int64_t threads = n * (hdim / 8);
+  if (threads == 0) return hipSuccess;
+  gather_rows_kernel<<<grid1(threads, 256), 256, 0, s>>>(h, perm, cnt, hdim, out, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_split(const float* h, const int* perm, const int* cnt, int64_t n,
+                               int64_t hdim, uint16_t* hi, uint16_t* lo, hipStream_t s) {
+  const int64_t threads = n * (hdim / 8);
+  if (threads == 0) return hipSuccess;
+  gather_split_kernel<<<grid1(threads, 256), 256, 0, s>>>(h, perm, cnt, hdim, hi, lo, n);
   return hipGetLastError();
 }
 

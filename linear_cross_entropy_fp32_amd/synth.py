@@ -23,6 +23,10 @@ bit-identical tensors):
   * targets uniform in [0, V) or bounded Zipf(a): P(k) proportional to
     (k+1)^-a for k in [0, V), sampled by inverse CDF from float64 uniforms;
   * every 17th position (n % 17 == 0) is set to the ignore index -100;
+  * with prompt masking (the SFT-style workload), the first
+    round(prompt_frac * prompt_block) positions of every block of prompt_block
+    positions are set to -100 as well, as a completion-only loss masks the
+    prompt;
   * per-token grad_out ~ U[0, 2) for reduction "none".
 """
 from __future__ import annotations
@@ -49,6 +53,8 @@ class Workload:
     targets: str = "uniform"          # "uniform", "zipf", "all_ignored", "argmax" (set later)
     zipf_a: float = 1.1
     ignore_every: int = 17            # 0: nothing ignored
+    prompt_frac: float = 0.0          # share of each prompt_block masked at its start
+    prompt_block: int = 512
     reduction: str = "mean"           # "mean", "sum", "none"
     seed: int = 0
 
@@ -71,6 +77,10 @@ WORKLOADS = {
     "fp32_hidden_all_ignored": Workload("fp32_hidden_all_ignored", 16384, 4096, 151936,
                                         hidden_dtype="f32", targets="all_ignored",
                                         seed=1006),
+    # huge_vocab with 70% of every 512-token block masked as prompt (30% of
+    # the positions carry a loss): the case that valid-row compaction is for
+    "huge_vocab_sft": Workload("huge_vocab_sft", 2048, 640, 262144, softcap=30.0,
+                               ignore_every=0, prompt_frac=0.7, seed=1007),
 }
 
 
@@ -113,6 +123,10 @@ def make_inputs(w: Workload, n_tokens: Optional[int] = None) -> Inputs:
         raise ValueError(f"unknown target distribution {w.targets}")
     if w.ignore_every > 0:
         targets[:: w.ignore_every] = IGNORE_INDEX
+    if w.prompt_frac > 0:
+        masked = int(round(w.prompt_frac * w.prompt_block))
+        pos = torch.arange(n) % w.prompt_block
+        targets[pos < masked] = IGNORE_INDEX
     if w.targets == "all_ignored":
         targets[:] = IGNORE_INDEX
     if w.reduction == "none":

@@ -41,18 +41,21 @@ def prob_of(w: synth.Workload, mean_divisor: float = 0.0) -> Problem:
 
 
 def run_gpu(w: synth.Workload, inp: synth.Inputs, mean_divisor: float = 0.0,
-            backward: bool = True, dev: str = "cuda:0") -> dict:
-    """Forward (+ backward) through the C ABI; returns CPU tensors."""
+            backward: bool = True, dev: str = "cuda:0", compact: bool = False) -> dict:
+    """Forward (+ backward) through the C ABI; returns CPU tensors.  compact:
+    with valid-row compaction (flce_problem.compact_valid)."""
     h = inp.hidden.to(dev)
     wt = inp.weight.to(dev)
     b = None if inp.bias is None else inp.bias.to(dev)
     t = inp.targets.to(dev)
-    f = flce.flce_forward(h, wt, t, b, w.logit_scale, w.softcap, -100, mean_divisor)
+    f = flce.flce_forward(h, wt, t, b, w.logit_scale, w.softcap, -100, mean_divisor,
+                          compact_valid=compact)
     out = {k: (v.cpu() if v is not None else None) for k, v in f.items()}
     if backward:
         go = inp.grad_out.to(dev).reshape(-1)
         gh, gw, gb = flce.flce_backward(h, wt, t, f["lse"], f["reduced_i64"], MODES[w.reduction],
-                                        go, b, w.logit_scale, w.softcap, -100, mean_divisor)
+                                        go, b, w.logit_scale, w.softcap, -100, mean_divisor,
+                                        compact_valid=compact)
         out["grad_hidden"] = gh.cpu()
         out["grad_weight"] = gw.cpu()
         out["grad_bias"] = None if gb is None else gb.cpu()
@@ -82,6 +85,22 @@ def check_tokens(g: dict, o: dict, rows=None, label: str = "") -> None:
         assert np.all(g["loss"].numpy()[sel][~valid] == 0)
         assert np.all(g["entropy"].numpy()[sel][~valid] == 0)
     assert np.array_equal(ghit[sure], o["hit"][sure]), f"{label} hit differs on sure rows"
+
+
+def check_compact_tokens(g: dict, o: dict, valid: np.ndarray, label: str = "") -> None:
+    """With valid-row compaction: the rows that carry a loss as check_tokens;
+    the other rows hold the documented fill (loss, entropy, hit, lse 0,
+    argmax -1)."""
+    idx = np.nonzero(valid)[0]
+    sub = {k: (o[k][idx] if isinstance(o[k], np.ndarray) and o[k].shape[:1] == valid.shape
+               else o[k]) for k in ("loss", "entropy", "lse", "argmax", "hit", "margin")}
+    sub["valid"] = np.ones(len(idx), dtype=bool)
+    check_tokens(g, sub, rows=idx, label=label)
+    skip = ~valid
+    for k in ("loss", "entropy", "lse"):
+        assert np.all(g[k].numpy()[skip] == 0), f"{label} {k} not 0 on a skipped row"
+    assert np.all(g["hit"].numpy()[skip] == 0), f"{label} hit set on a skipped row"
+    assert np.all(g["argmax"].numpy()[skip] == -1), f"{label} argmax not -1 on a skipped row"
 
 
 def check_reduced(g: dict, o: dict, label: str = "") -> None:

@@ -81,10 +81,23 @@ def test_validate(kw, code):
         assert flce.flce_workspace_bytes(p) > 0
 
 
-def test_reserved_field_must_be_zero():
+def test_compact_flag_is_zero_or_one():
     p = flce.make_problem(4, 64, 10)
-    p.reserved = 1
-    assert flce.flce_validate(p) == -7
+    for value, rc in ((0, 0), (1, 0), (2, -7), (-1, -7)):
+        p.compact_valid = value
+        assert flce.flce_validate(p) == rc, value
+
+
+def test_compact_workspace_adds_rows_only():
+    """Row compaction adds per-row state (perm, counts, compact bf16 hidden
+    rows) and the grad_hidden slot; nothing that grows with N x V."""
+    for n, h, v, dt in ((2048, 640, 262144, flce.FLCE_BF16), (16384, 4096, 151936, flce.FLCE_F32),
+                        (5, 8, 3, flce.FLCE_BF16)):
+        base = flce.flce_workspace_bytes(flce.make_problem(n, h, v, hidden_dtype=dt))
+        comp = flce.flce_workspace_bytes(flce.make_problem(n, h, v, hidden_dtype=dt,
+                                                           compact_valid=True))
+        extra = comp - base
+        assert 0 <= extra <= n * 4 + 8 + 2 * (n // 256 + 1) * 4 + n * h * 2 + n * h * 4 + 4 * 256
 
 
 def test_workspace_is_bounded():

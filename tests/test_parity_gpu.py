@@ -269,7 +269,8 @@ def test_autograd_wrapper_matches_c_abi():
 
 # ------------------------------------------------------- full-size workloads
 
-FULL = ["tiny", "huge_vocab", "bias_none", "zipf_sum", "fp32_hidden", "fp32_hidden_all_ignored"]
+FULL = ["tiny", "huge_vocab", "bias_none", "zipf_sum", "fp32_hidden", "fp32_hidden_all_ignored",
+        "huge_vocab_sft"]
 
 
 @pytest.mark.parametrize("name", FULL)
