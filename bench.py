@@ -35,6 +35,10 @@ def parse():
                     help="after the timed steps, this many steps each preceded (outside their "
                          "event bracket) by a 512 MiB write that evicts L2 and MALL; 0 = none")
     ap.add_argument("--workload", default="huge_vocab")
+    ap.add_argument("--compact", action="store_true",
+                    help="valid-row compaction (flce_problem.compact_valid): only the rows that "
+                         "carry a loss are projected; tokens/s still counts every position, and "
+                         "the flop figures count the valid rows")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -231,7 +235,7 @@ def main() -> int:
     t = inp.targets.to(dev)
     go = inp.grad_out.to(dev).reshape(-1)
     n, hd, v = w.n_tokens, w.hidden, w.vocab
-    prob = _binding.problem_for(h, wt, w.logit_scale, w.softcap)
+    prob = _binding.problem_for(h, wt, w.logit_scale, w.softcap, compact_valid=args.compact)
     ws_bytes = flce.flce_workspace_bytes(prob)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     f32 = dict(dtype=torch.float32, device=dev)
@@ -335,7 +339,9 @@ def main() -> int:
         for i in range(2 * args.cold_steps):
             hip.hipEventDestroy(ctypes.c_void_p(cev[i]))
         del flush
-    flops = 8.0 * n * hd * v
+    # with compaction the algorithmic work is that of the rows carrying a loss
+    n_work = int(red_i[0].item()) if args.compact else n
+    flops = 8.0 * n_work * hd * v
     tflops = flops / (ms * 1e-3) / 1e12
     # dominant kernel: the backward contraction (grad_hidden and grad_weight of
     # one vocabulary chunk per launch); over a step its launches do 4*N*H*V
@@ -343,7 +349,7 @@ def main() -> int:
     launches = max(1, len(kern_ms))
     kern_avg = sum(kern_ms) / launches if kern_ms else float("nan")
     per_step_ms = kern_avg * launches / args.steps
-    kern_tflops = 4.0 * n * hd * v / (per_step_ms * 1e-3) / 1e12
+    kern_tflops = 4.0 * n_work * hd * v / (per_step_ms * 1e-3) / 1e12
     traffic = _committed_traffic(w.name, "contract_kernel")
     out = {
         "metric": METRIC, "value": n / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1,
@@ -352,7 +358,8 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": w.name, "n_tokens": n, "hidden": hd, "vocab": v,
                    "hidden_dtype": w.hidden_dtype, "bias": w.bias, "logit_scale": w.logit_scale,
-                   "softcap": w.softcap, "reduction": w.reduction},
+                   "softcap": w.softcap, "reduction": w.reduction,
+                   "compact_valid": bool(args.compact), "n_valid": int(red_i[0].item())},
         "tflops": tflops, "pct_bf16_peak": 100.0 * tflops / PEAK_BF16_TFLOPS,
         "fwd_ms": fwd_ms, "bwd_ms": bwd_ms, "wall_s": wall,
         "step_ms_p20_p50_p80": [float(np.percentile(step_ms, q)) for q in (20, 50, 80)],
