@@ -120,7 +120,11 @@ Plan make_plan(const flce_problem* p) {
   pl.vc = vc;
   pl.n_chunks = (int)cdiv(v, vc);
   const int64_t chunk_tiles = vc / kLogitTileV;
-  pl.dz_tiles_per_wg = (int)std::max<int64_t>(1, chunk_tiles * pl.n_tok_tiles / kDzWgs);
+  // with the row compaction only the valid rows' token tiles have work, so
+  // the workgroups take half as many tiles each: twice as many workgroups,
+  // which keeps the GPU filled when a third of the rows carry a loss
+  pl.dz_tiles_per_wg = (int)std::max<int64_t>(
+      1, chunk_tiles * pl.n_tok_tiles / kDzWgs / (p->compact_valid ? 2 : 1));
   // grad_hidden split: its workgroups get twice the K depth of the
   // grad_weight ones (N); the launch interleaves the two kinds so every XCD
   // gets the same mix, and fewer splits mean fewer partial slots to update
