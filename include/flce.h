@@ -45,7 +45,7 @@ extern "C" {
 #define FLCE_ERR_NULL (-1)      /* a required pointer is null */
 #define FLCE_ERR_SHAPE (-2)     /* N < 0, H < 8, H % 8 != 0, V < 1, or a size too large:
                                    N < 2^23, N*H < 2^30, V*H < 2^31, H <= 2^20, V <= 2^30 */
-#define FLCE_ERR_DTYPE (-3)     /* unsupported dtype combination (weight must be bf16) */
+#define FLCE_ERR_DTYPE (-3)     /* a dtype code other than FLCE_BF16 / FLCE_F32 */
 #define FLCE_ERR_ALIGN (-4)     /* a pointer is not aligned as documented */
 #define FLCE_ERR_WORKSPACE (-5) /* workspace smaller than flce_workspace_bytes() */
 #define FLCE_ERR_HIP (-6)       /* a kernel launch failed */
@@ -63,7 +63,12 @@ typedef struct flce_problem {
   int64_t hidden;        /* H >= 8, H % 8 == 0                                    */
   int64_t vocab;         /* V >= 1 rows of weight                                 */
   int32_t hidden_dtype;  /* FLCE_BF16 or FLCE_F32 (fp32 hidden states)            */
-  int32_t weight_dtype;  /* FLCE_BF16 (the lm_head is cast to bf16 by the caller) */
+  int32_t weight_dtype;  /* FLCE_BF16, or FLCE_F32 (an fp32 lm_head, e.g. an fp32
+                            master weight: it is split on the device into bf16
+                            high and low parts, and the logits take
+                            W_hi.h + W_lo.h, plus W_hi.h_lo with fp32 hidden,
+                            which keeps them at fp32 accuracy; grad_hidden
+                            takes W_hi.  The split needs 4*V*H workspace bytes.) */
   float logit_scale;     /* s, finite; 1 = off                                    */
   float softcap;         /* c, final_logit_softcapping; <= 0 = off                */
   int64_t ignore_index;  /* usually -100                                          */
@@ -90,7 +95,7 @@ int flce_workspace_bytes(const flce_problem* p, size_t* bytes);
 
 /* Forward.
  *   hidden   [N, H]  bf16 or fp32 (per p->hidden_dtype), 16-byte aligned
- *   weight   [V, H]  bf16, 16-byte aligned
+ *   weight   [V, H]  bf16 or fp32 (per p->weight_dtype), 16-byte aligned
  *   bias     [V]     fp32, or NULL for no bias
  *   targets  [N]     int64; ignore_index marks ignored rows; a value outside
  *                    [0, V) that is not ignore_index is treated as ignored and

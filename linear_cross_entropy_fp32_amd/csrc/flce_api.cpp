@@ -66,6 +66,7 @@ struct Plan {
   // row compaction: perm [N] int32, cnt [2] int32, block scratch, compact
   // bf16 hidden rows [N, H] (fp32 hidden: the hi / lo split rows instead)
   size_t off_perm, off_cnt, off_blk, off_hc;
+  size_t off_wsplit;     // fp32 lm_head: its bf16 hi / lo split [2, V, H]
   size_t fwd_bytes, bwd_bytes, bytes;
 };
 
@@ -84,9 +85,8 @@ int validate(const flce_problem* p) {
     return fail(FLCE_ERR_SHAPE, "N*H must stay below 2^30 and V*H below 2^31 elements");
   if (p->hidden_dtype != FLCE_BF16 && p->hidden_dtype != FLCE_F32)
     return fail(FLCE_ERR_DTYPE, "hidden_dtype=%d unsupported (bf16 or fp32)", p->hidden_dtype);
-  if (p->weight_dtype != FLCE_BF16)
-    return fail(FLCE_ERR_DTYPE, "weight_dtype=%d unsupported: the lm_head must be bf16",
-                p->weight_dtype);
+  if (p->weight_dtype != FLCE_BF16 && p->weight_dtype != FLCE_F32)
+    return fail(FLCE_ERR_DTYPE, "weight_dtype=%d unsupported (bf16 or fp32)", p->weight_dtype);
   if (!std::isfinite(p->logit_scale))
     return fail(FLCE_ERR_ARG, "logit_scale must be finite");
   if (std::isnan(p->softcap) || std::isinf(p->softcap))
@@ -135,6 +135,8 @@ Plan make_plan(const flce_problem* p) {
   pl.gh_splits = (int)cdiv(width, pl.gh_kps);
 
   size_t off = 0;
+  pl.off_wsplit = off;
+  if (p->weight_dtype == FLCE_F32) off += aup(size_t(2) * v * h * 2);
   pl.off_hsplit = off;
   if (p->hidden_dtype == FLCE_F32) off += aup(size_t(2) * n * h * 2);
   pl.off_perm = pl.off_cnt = pl.off_blk = pl.off_hc = off;
@@ -217,6 +219,8 @@ int hip_check(hipError_t e, const char* what) {
 // for: perm, the device count of compact rows, and the device count of the
 // out-of-range targets it leaves out (all null without compaction).
 struct Rows {
+  const uint16_t* w0 = nullptr;   // lm_head (bf16), or the high part of an fp32 one
+  const uint16_t* w1 = nullptr;   // the low part of an fp32 lm_head, else null
   const uint16_t* h0 = nullptr;
   const uint16_t* h1 = nullptr;
   const int* perm = nullptr;
@@ -224,11 +228,22 @@ struct Rows {
   const int* n_bad = nullptr;
 };
 
-int prepare_rows(const flce_problem* p, const Plan& pl, const void* hidden,
+int prepare_rows(const flce_problem* p, const Plan& pl, const void* hidden, const void* weight,
                  const int64_t* targets, char* ws, hipStream_t s, Rows& r) {
   const int64_t n = p->n_tokens, h = p->hidden;
   int rc;
   r = Rows{};
+  r.w0 = static_cast<const uint16_t*>(weight);
+  if (p->weight_dtype == FLCE_F32) {
+    uint16_t* whi = reinterpret_cast<uint16_t*>(ws + pl.off_wsplit);
+    uint16_t* wlo = whi + p->vocab * h;
+    if ((rc = hip_check(launch_split_hidden(static_cast<const float*>(weight), whi, wlo,
+                                            p->vocab * h, s),
+                        "split_weight")))
+      return rc;
+    r.w0 = whi;
+    r.w1 = wlo;
+  }
   r.h0 = static_cast<const uint16_t*>(hidden);
   if (n == 0) return FLCE_OK;
   uint16_t* hi = reinterpret_cast<uint16_t*>(ws + pl.off_hsplit);
@@ -337,11 +352,12 @@ int flce_forward(const flce_problem* p, const void* hidden, const void* weight,
   char* ws = static_cast<char*>(workspace);
 
   Rows rows;
-  if ((rc = prepare_rows(p, pl, hidden, targets, ws, s, rows))) return rc;
+  if ((rc = prepare_rows(p, pl, hidden, weight, targets, ws, s, rows))) return rc;
   PartState* part = reinterpret_cast<PartState*>(ws + pl.off_part);
   if (n > 0) {
     FwdArgs a{};
-    a.w = static_cast<const uint16_t*>(weight);
+    a.w = rows.w0;
+    a.w1 = rows.w1;
     a.h0 = rows.h0;
     a.h1 = rows.h1;
     a.bias = bias;
@@ -424,7 +440,7 @@ int flce_backward(const flce_problem* p, const void* hidden, const void* weight,
   }
 
   Rows rows;
-  if ((rc = prepare_rows(p, pl, hidden, targets, ws, s, rows))) return rc;
+  if ((rc = prepare_rows(p, pl, hidden, weight, targets, ws, s, rows))) return rc;
   const uint16_t* h0 = rows.h0;
   const uint16_t* h1 = rows.h1;
   const bool slots = pl.gh_splits > 1 || rows.perm != nullptr;   // grad_hidden via the slots
@@ -432,7 +448,8 @@ int flce_backward(const flce_problem* p, const void* hidden, const void* weight,
   float* ghpart = reinterpret_cast<float*>(ws + pl.off_ghpart);
 
   DzArgs d{};
-  d.w = static_cast<const uint16_t*>(weight);
+  d.w = rows.w0;
+  d.w1 = rows.w1;
   d.h0 = h0;
   d.h1 = h1;
   d.bias = bias;
@@ -479,7 +496,7 @@ int flce_backward(const flce_problem* p, const void* hidden, const void* weight,
                         "bwd_dz")))
       return rc;
 
-    g.w = static_cast<const uint16_t*>(weight) + c0 * h;
+    g.w = rows.w0 + c0 * h;   // an fp32 lm_head enters grad_hidden as its high part
     g.width = (int)width;
     g.gh_accumulate = c > 0;
     g.gw = grad_weight + c0 * h;

@@ -31,7 +31,8 @@ struct BlockSums {
 };
 
 struct FwdArgs {
-  const uint16_t* w;     // [V, H] bf16
+  const uint16_t* w;     // [V, H] bf16 (lm_head, or its high part)
+  const uint16_t* w1;    // [V, H] bf16 low part of an fp32 lm_head, or null
   const uint16_t* h0;    // [N, H] bf16 (hidden, or its high part)
   const uint16_t* h1;    // [N, H] bf16 low part of an fp32 hidden, or null
   const float* bias;     // [V] or null
@@ -65,7 +66,8 @@ struct FinalArgs {
 };
 
 struct DzArgs {
-  const uint16_t* w;
+  const uint16_t* w;     // [V, H] bf16 (lm_head, or its high part)
+  const uint16_t* w1;    // [V, H] bf16 low part of an fp32 lm_head, or null
   const uint16_t* h0;
   const uint16_t* h1;
   const float* bias;

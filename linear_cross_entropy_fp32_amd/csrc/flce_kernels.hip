@@ -297,6 +297,16 @@ __global__ void gather_split_kernel(const float* __restrict__ h, const int* __re
   *reinterpret_cast<u32x4*>(lo + c * hdim + k) = pl;
 }
 
+// The K-loop segments of a logit tile: W . h, plus W . h_lo for fp32 hidden
+// and W_lo . h for an fp32 lm_head (h_lo . W_lo, below 2^-16 of the product,
+// is left out).
+__device__ __forceinline__ SegPlan logit_segments(bool h_split, bool w_split) {
+  if (h_split && w_split) return SegPlan{3, 0b100, 0b010};
+  if (h_split) return SegPlan{2, 0, 0b10};
+  if (w_split) return SegPlan{2, 0b10, 0};
+  return SegPlan{1, 0, 0};
+}
+
 // ------------------------------------------------------------- forward: K1
 // Fold one token column (kQ values in a lane) of a finished logit tile into
 // that token's state.  `val` holds the values in place of the accumulators.
@@ -400,7 +410,7 @@ struct FwdEpilogue {
 // into the per-token states held in registers.  At the end of the split the
 // states of the two half-waves and of the two waves sharing a token are merged
 // and written as one partial state per (split, token).
-template <bool CAP, bool FIXED, bool BIAS>
+template <bool CAP, bool FIXED, bool BIAS, bool WSPLIT>
 __global__ void __launch_bounds__(kThreads, 2)
 fwd_stats_kernel(const FwdArgs a) {
   __shared__ __attribute__((aligned(16))) char lds[LogitTile::kLdsBytes];
@@ -425,12 +435,14 @@ fwd_stats_kernel(const FwdArgs a) {
   }
   const int vt_begin = sp * a.tiles_per_split;
   const int ntiles = min(a.n_voc_tiles, vt_begin + a.tiles_per_split) - vt_begin;
-  const Operand opA{a.w, a.hdim, vt_begin * kLogitTileV, a.v, a.hdim};
+  const Operand opA0{a.w, a.hdim, vt_begin * kLogitTileV, a.v, a.hdim};
+  const Operand opA1{a.w1 ? a.w1 : a.w, a.hdim, vt_begin * kLogitTileV, a.v, a.hdim};
   const Operand opB0{a.h0, a.hdim, n0, n_rows, a.hdim};
   const Operand opB1{a.h1 ? a.h1 : a.h0, a.hdim, n0, n_rows, a.hdim};
   FwdEpilogue<CAP, FIXED, BIAS> epi{a, st, tgt, vt_begin, wm, half};
   LogitTile T;
-  T.run_stream(lds, opA, opB0, opB1, a.h1 != nullptr, a.hdim, ntiles, epi);
+  T.run_stream<WSPLIT>(lds, opA0, opA1, opB0, opB1,
+                       logit_segments(a.h1 != nullptr, WSPLIT), a.hdim, ntiles, epi);
 
 #pragma unroll
   for (int j = 0; j < kColumns; ++j) {
@@ -708,7 +720,7 @@ struct DzEpilogue {
   }
 };
 
-template <bool CAP, bool BIAS>
+template <bool CAP, bool BIAS, bool WSPLIT>
 __global__ void __launch_bounds__(kThreads, 2)
 bwd_dz_kernel(const DzArgs a) {
   __shared__ __attribute__((aligned(16))) char lds[LogitTile::kLdsBytes];
@@ -737,13 +749,15 @@ bwd_dz_kernel(const DzArgs a) {
   }
   const int vt_begin = grp * a.tiles_per_wg;
   const int ntiles = min(a.chunk_tiles, vt_begin + a.tiles_per_wg) - vt_begin;
-  const Operand opA{a.w, a.hdim, a.c0 + vt_begin * kLogitTileV, a.v, a.hdim};
+  const Operand opA0{a.w, a.hdim, a.c0 + vt_begin * kLogitTileV, a.v, a.hdim};
+  const Operand opA1{a.w1 ? a.w1 : a.w, a.hdim, a.c0 + vt_begin * kLogitTileV, a.v, a.hdim};
   const Operand opB0{a.h0, a.hdim, n0, n_rows, a.hdim};
   const Operand opB1{a.h1 ? a.h1 : a.h0, a.hdim, n0, n_rows, a.hdim};
   DzEpilogue<CAP, BIAS> epi{a, gs, nl, tgt, vt_begin, wm, half,
                            __builtin_amdgcn_readfirstlane(n0 + wn * (kLogitTileN / 2))};
   LogitTile T;
-  T.run_stream(lds, opA, opB0, opB1, a.h1 != nullptr, a.hdim, ntiles, epi);
+  T.run_stream<WSPLIT>(lds, opA0, opA1, opB0, opB1,
+                       logit_segments(a.h1 != nullptr, WSPLIT), a.hdim, ntiles, epi);
 }
 
 // ------------------------------------------- contractions over a dz chunk
@@ -935,7 +949,11 @@ hipError_t launch_fwd_stats(const FwdArgs& a, bool cap, bool fixed_ref, hipStrea
   const unsigned grid = (unsigned)(a.n_tok_tiles * a.n_splits);
   if (grid == 0) return hipSuccess;
   const bool bias = a.bias != nullptr;
-#define FLCE_FWD(C, F, B) fwd_stats_kernel<C, F, B><<<grid, kThreads, 0, s>>>(a)
+#define FLCE_FWD(C, F, B)                                               \
+  do {                                                                  \
+    if (a.w1) fwd_stats_kernel<C, F, B, true><<<grid, kThreads, 0, s>>>(a); \
+    else fwd_stats_kernel<C, F, B, false><<<grid, kThreads, 0, s>>>(a);     \
+  } while (0)
   if (cap && fixed_ref) {
     if (bias) FLCE_FWD(true, true, true); else FLCE_FWD(true, true, false);
   } else if (cap) {
@@ -961,13 +979,17 @@ hipError_t launch_bwd_dz(const DzArgs& a, bool cap, hipStream_t s) {
   const unsigned grid = (unsigned)(a.n_tok_tiles * groups);
   if (grid == 0) return hipSuccess;
   const bool bias = a.bias != nullptr;
+#define FLCE_DZ(C, B)                                                \
+  do {                                                               \
+    if (a.w1) bwd_dz_kernel<C, B, true><<<grid, kThreads, 0, s>>>(a); \
+    else bwd_dz_kernel<C, B, false><<<grid, kThreads, 0, s>>>(a);     \
+  } while (0)
   if (cap) {
-    if (bias) bwd_dz_kernel<true, true><<<grid, kThreads, 0, s>>>(a);
-    else bwd_dz_kernel<true, false><<<grid, kThreads, 0, s>>>(a);
+    if (bias) FLCE_DZ(true, true); else FLCE_DZ(true, false);
   } else {
-    if (bias) bwd_dz_kernel<false, true><<<grid, kThreads, 0, s>>>(a);
-    else bwd_dz_kernel<false, false><<<grid, kThreads, 0, s>>>(a);
+    if (bias) FLCE_DZ(false, true); else FLCE_DZ(false, false);
   }
+#undef FLCE_DZ
   return hipGetLastError();
 }
 

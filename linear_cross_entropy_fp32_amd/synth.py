@@ -19,7 +19,8 @@ bit-identical tensors):
   * one CPU ``torch.Generator`` per workload, seeded with ``seed``;
   * draw order: hidden, weight, bias, targets, grad_out;
   * hidden ~ N(0, 1), weight ~ N(0, 0.02), bias ~ N(0, 0.1), drawn in float32
-    and rounded to bfloat16 (round-to-nearest-even) where the dtype is bf16;
+    and rounded to bfloat16 (round-to-nearest-even) where the dtype is bf16
+    (hidden and weight each have their own dtype);
   * targets uniform in [0, V) or bounded Zipf(a): P(k) proportional to
     (k+1)^-a for k in [0, V), sampled by inverse CDF from float64 uniforms;
   * every 17th position (n % 17 == 0) is set to the ignore index -100;
@@ -47,6 +48,7 @@ class Workload:
     hidden: int
     vocab: int
     hidden_dtype: str = "bf16"        # "bf16" or "f32"
+    weight_dtype: str = "bf16"        # "bf16" or "f32" (an fp32 lm_head, not rounded)
     bias: bool = False
     logit_scale: float = 1.0
     softcap: float = 0.0              # <= 0: no softcapping
@@ -81,6 +83,10 @@ WORKLOADS = {
     # the positions carry a loss): the case that valid-row compaction is for
     "huge_vocab_sft": Workload("huge_vocab_sft", 2048, 640, 262144, softcap=30.0,
                                ignore_every=0, prompt_frac=0.7, seed=1007),
+    # huge_vocab with an fp32 lm_head (an fp32 master weight, as under FSDP2
+    # mixed precision)
+    "huge_vocab_fp32_lm_head": Workload("huge_vocab_fp32_lm_head", 2048, 640, 262144,
+                                        softcap=30.0, weight_dtype="f32", seed=1008),
 }
 
 
@@ -110,8 +116,11 @@ def make_inputs(w: Workload, n_tokens: Optional[int] = None) -> Inputs:
         hidden = hidden.to(torch.bfloat16)
     elif w.hidden_dtype != "f32":
         raise ValueError(f"unknown hidden dtype {w.hidden_dtype}")
-    weight = (torch.randn(w.vocab, w.hidden, generator=gen, dtype=torch.float32) * 0.02
-              ).to(torch.bfloat16)
+    weight = torch.randn(w.vocab, w.hidden, generator=gen, dtype=torch.float32) * 0.02
+    if w.weight_dtype == "bf16":
+        weight = weight.to(torch.bfloat16)
+    elif w.weight_dtype != "f32":
+        raise ValueError(f"unknown weight dtype {w.weight_dtype}")
     bias = None
     if w.bias:
         bias = torch.randn(w.vocab, generator=gen, dtype=torch.float32) * 0.1

@@ -63,7 +63,8 @@ def test_struct_layout_matches_header(tmp_path):
     (dict(n_tokens=(1 << 18) - 1, hidden=1 << 12, vocab=10), 0),
     (dict(n_tokens=4, hidden=1 << 12, vocab=1 << 19), -2),
     (dict(n_tokens=4, hidden=1 << 12, vocab=(1 << 19) - 1), 0),
-    (dict(n_tokens=4, hidden=64, vocab=10, weight_dtype=1), -3),
+    (dict(n_tokens=4, hidden=64, vocab=10, weight_dtype=2), -3),
+    (dict(n_tokens=4, hidden=64, vocab=10, weight_dtype=1), 0),
     (dict(n_tokens=4, hidden=64, vocab=10, hidden_dtype=7), -3),
     (dict(n_tokens=4, hidden=64, vocab=10, logit_scale=float("nan")), -7),
     (dict(n_tokens=4, hidden=64, vocab=10, softcap=float("inf")), -7),

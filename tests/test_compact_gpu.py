@@ -52,6 +52,8 @@ CASES = [
                          reduction="sum", prompt_frac=0.3, prompt_block=100),
     synth.small_workload(64, 128, 1, 36),                                # V = 1
     synth.small_workload(260, 64, 900, 37, targets="all_ignored", hidden_dtype="f32"),
+    synth.small_workload(800, 96, 2000, 42, weight_dtype="f32", hidden_dtype="f32",
+                         prompt_frac=0.6, prompt_block=200, softcap=30.0),
 ]
 
 

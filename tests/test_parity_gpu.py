@@ -49,6 +49,11 @@ SMALL = [
     # softcap above 120 / (2 log2 e): the forward keeps a running reference
     synth.small_workload(180, 96, 2100, 24, softcap=50.0, logit_scale=20.0, bias=True),
     synth.small_workload(300, 64, 1700, 25, softcap=60.0, logit_scale=8.0, reduction="none"),
+    # fp32 lm_head (split into bf16 high + low parts on the device)
+    synth.small_workload(290, 72, 2300, 27, weight_dtype="f32", softcap=30.0, bias=True),
+    synth.small_workload(260, 136, 1900, 28, weight_dtype="f32", hidden_dtype="f32",
+                         reduction="none"),
+    synth.small_workload(4100, 64, 30000, 29, weight_dtype="f32", logit_scale=2.0),
 ]
 
 
@@ -270,7 +275,7 @@ def test_autograd_wrapper_matches_c_abi():
 # ------------------------------------------------------- full-size workloads
 
 FULL = ["tiny", "huge_vocab", "bias_none", "zipf_sum", "fp32_hidden", "fp32_hidden_all_ignored",
-        "huge_vocab_sft"]
+        "huge_vocab_sft", "huge_vocab_fp32_lm_head"]
 
 
 @pytest.mark.parametrize("name", FULL)
