@@ -155,11 +155,13 @@ def test_compact_autograd_wrapper():
                    res[0][2].numpy().astype(np.float64)) <= 1e-2
 
 
-def test_fullsize_sft_compact_against_stored_oracle():
-    """huge_vocab with 70% prompt masking, compacted, in the bench's launch
-    configuration, against oracle values written by
-    tests/golden/make_fullsize_golden.py."""
-    name = "huge_vocab_sft"
+@pytest.mark.parametrize("name", ["huge_vocab_sft", "bias_none", "zipf_sum", "fp32_hidden",
+                                  "fp32_hidden_all_ignored", "huge_vocab_fp32_lm_head"])
+def test_fullsize_compact_against_stored_oracle(name):
+    """Full-size workloads, compacted, in the bench's launch configuration,
+    against oracle values written by tests/golden/make_fullsize_golden.py
+    (huge_vocab_sft: 70% prompt masking; the others ignore every 17th row,
+    or every row)."""
     path = os.path.join(GOLDEN, f"fullsize_{name}.npz")
     gold = np.load(path, allow_pickle=False)
     w = synth.WORKLOADS[name]
@@ -177,3 +179,8 @@ def test_fullsize_sft_compact_against_stored_oracle():
     rows, vrows = gold["rows"], gold["vocab_rows"]
     check_grad(g["grad_hidden"].numpy()[rows], gold["grad_hidden_rows"], "grad_hidden rows", name)
     check_grad(g["grad_weight"].numpy()[vrows], gold["grad_weight_rows"], "grad_weight rows", name)
+    if inp.bias is not None:
+        check_grad(g["grad_bias"].numpy()[vrows], gold["grad_bias_rows"], "grad_bias rows", name)
+    if o["n_valid"] == 0:
+        for k in ("grad_hidden", "grad_weight"):
+            assert torch.count_nonzero(g[k]).item() == 0, k
