@@ -110,6 +110,8 @@ struct ContractArgs {
   const int* n_dev;      // row compaction: only dz rows c < *n_dev are used; else null
 };
 
+// hi = bf16(h), lo = bf16(h - hi) for count values (a multiple of 8; the
+// pointers 16-byte aligned): fp32 hidden states or an fp32 lm_head.
 hipError_t launch_split_hidden(const float* h, uint16_t* hi, uint16_t* lo, int64_t count,
                                hipStream_t s);
 hipError_t launch_fwd_stats(const FwdArgs& a, bool cap, bool fixed_ref, hipStream_t s);

@@ -133,22 +133,27 @@ __device__ __forceinline__ void load_bias(const float* bias, int v, int vw, floa
 // --------------------------------------------------- fp32 hidden: hi / lo split
 // h = hi + lo with hi = bf16(h), lo = bf16(h - hi); the lm_head is exact in
 // bf16, so two bf16 MFMA passes reproduce the fp32 product to ~2^-17.
+// Eight values per thread (count is a multiple of 8: rows of H values, H % 8
+// == 0), read and written 16 bytes at a time.
 __global__ void split_hidden_kernel(const float* __restrict__ h, uint16_t* __restrict__ hi,
                                     uint16_t* __restrict__ lo, int64_t count) {
-  const int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 2;
+  const int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 8;
   if (i >= count) return;
-  const float a = h[i];
-  const float b = (i + 1 < count) ? h[i + 1] : 0.f;
-  const uint32_t ph = pack_bf16x2(a, b);
-  const float ah = __builtin_bit_cast(float, ph << 16);
-  const float bh = __builtin_bit_cast(float, ph & 0xffff0000u);
-  const uint32_t pl = pack_bf16x2(a - ah, b - bh);
-  hi[i] = (uint16_t)(ph & 0xffffu);
-  lo[i] = (uint16_t)(pl & 0xffffu);
-  if (i + 1 < count) {
-    hi[i + 1] = (uint16_t)(ph >> 16);
-    lo[i + 1] = (uint16_t)(pl >> 16);
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
+  const f32x4 x0 = *reinterpret_cast<const f32x4*>(h + i);
+  const f32x4 x1 = *reinterpret_cast<const f32x4*>(h + i + 4);
+  const float v[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+  u32x4 ph, pl;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float a = v[2 * k], b = v[2 * k + 1];
+    ph[k] = pack_bf16x2(a, b);
+    const float ah = __builtin_bit_cast(float, ph[k] << 16);
+    const float bh = __builtin_bit_cast(float, ph[k] & 0xffff0000u);
+    pl[k] = pack_bf16x2(a - ah, b - bh);
   }
+  *reinterpret_cast<u32x4*>(hi + i) = ph;
+  *reinterpret_cast<u32x4*>(lo + i) = pl;
 }
 
 // ------------------------------------------------------------ row compaction
@@ -941,7 +946,8 @@ static inline unsigned grid1(int64_t count, int block) {
 hipError_t launch_split_hidden(const float* h, uint16_t* hi, uint16_t* lo, int64_t count,
                                hipStream_t s) {
   if (count == 0) return hipSuccess;
-  split_hidden_kernel<<<grid1((count + 1) / 2, 256), 256, 0, s>>>(h, hi, lo, count);
+  if (count % 8 != 0) return hipErrorInvalidValue;   // whole rows of H % 8 == 0 values
+  split_hidden_kernel<<<grid1(count / 8, 256), 256, 0, s>>>(h, hi, lo, count);
   return hipGetLastError();
 }
 
