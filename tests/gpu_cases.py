@@ -36,26 +36,28 @@ def to_f64(t):
         if t.dtype != torch.float64 else t.detach().cpu().numpy()
 
 
-def prob_of(w: synth.Workload, mean_divisor: float = 0.0) -> Problem:
-    return Problem(logit_scale=w.logit_scale, softcap=w.softcap, mean_divisor=mean_divisor)
+def prob_of(w: synth.Workload, mean_divisor: float = 0.0, ignore_index: int = -100) -> Problem:
+    return Problem(logit_scale=w.logit_scale, softcap=w.softcap, mean_divisor=mean_divisor,
+                   ignore_index=ignore_index)
 
 
 def run_gpu(w: synth.Workload, inp: synth.Inputs, mean_divisor: float = 0.0,
-            backward: bool = True, dev: str = "cuda:0", compact: bool = False) -> dict:
+            backward: bool = True, dev: str = "cuda:0", compact: bool = False,
+            ignore_index: int = -100) -> dict:
     """Forward (+ backward) through the C ABI; returns CPU tensors.  compact:
     with valid-row compaction (flce_problem.compact_valid)."""
     h = inp.hidden.to(dev)
     wt = inp.weight.to(dev)
     b = None if inp.bias is None else inp.bias.to(dev)
     t = inp.targets.to(dev)
-    f = flce.flce_forward(h, wt, t, b, w.logit_scale, w.softcap, -100, mean_divisor,
+    f = flce.flce_forward(h, wt, t, b, w.logit_scale, w.softcap, ignore_index, mean_divisor,
                           compact_valid=compact)
     out = {k: (v.cpu() if v is not None else None) for k, v in f.items()}
     if backward:
         go = inp.grad_out.to(dev).reshape(-1)
         gh, gw, gb = flce.flce_backward(h, wt, t, f["lse"], f["reduced_i64"], MODES[w.reduction],
-                                        go, b, w.logit_scale, w.softcap, -100, mean_divisor,
-                                        compact_valid=compact)
+                                        go, b, w.logit_scale, w.softcap, ignore_index,
+                                        mean_divisor, compact_valid=compact)
         out["grad_hidden"] = gh.cpu()
         out["grad_weight"] = gw.cpu()
         out["grad_bias"] = None if gb is None else gb.cpu()
