@@ -34,8 +34,8 @@ constexpr int64_t kMaxElems = int64_t(1) << 31;      // V*H stays int32-indexabl
 // (N*width*2) must each stay below it.
 constexpr int64_t kMaxOperandBytes = (int64_t(1) << 31) - 1;
 constexpr size_t kAlign = 256;
-constexpr int64_t kTargetWgs = 2048;                 // ~8 workgroups per CU
-constexpr int64_t kDzWgs = 512;                      // dz workgroups per chunk: one round at two per CU
+constexpr int64_t kTargetWgs = 2048;                 // forward workgroups: ~8 per CU
+constexpr int64_t kDzWgs = 256 * kLogitWgsPerCu;     // dz workgroups per chunk: one round
 // bf16 dz of one backward vocab chunk.  A 128 MiB chunk stays in the 256 MB
 // last-level cache (MALL) between the dz write and the contraction's two
 // reads of it; it is used while it leaves the chunk at least kMinChunkWidth

@@ -5,12 +5,11 @@
 
 namespace flce {
 
-// Logit tiles (forward stats, backward dz): vocabulary rows x tokens.
-#ifndef FLCE_LOGIT_TILE_V
-#define FLCE_LOGIT_TILE_V 128
-#endif
-constexpr int kLogitTileV = FLCE_LOGIT_TILE_V;
-constexpr int kLogitTileN = 32768 / FLCE_LOGIT_TILE_V;
+// Logit tiles (forward stats, backward dz): 128 vocabulary rows x 256 tokens,
+// four waves in a 2 x 2 grid, two workgroups per CU.
+constexpr int kLogitTileV = 128;
+constexpr int kLogitTileN = 256;
+constexpr int kLogitWgsPerCu = 2;
 // Contraction tiles (grad_hidden, grad_weight): 256 x 128 outputs.
 constexpr int kGemmTileM = 256;
 constexpr int kGemmTileN = 128;

@@ -29,7 +29,7 @@ constexpr float kMasked = -3.0e38f;
 static_assert(kSliceK == kBK, "slice depth");
 static_assert(4 * 32 * (kLogitTileV / 2) * 2 <= Tile<kLogitTileV, kLogitTileN, true, true>::kStage,
               "dz transpose buffer fits one LDS stage");
-using LogitTile = Tile<kLogitTileV, kLogitTileN, true, true>;      // 128 x 256
+using LogitTile = Tile<kLogitTileV, kLogitTileN, true, true>;
 using GhTile = Tile<kGemmTileM, kGemmTileN, true, false>;          // dz . W
 using GwTile = Tile<kGemmTileM, kGemmTileN, false, false>;         // dz^T . h
 constexpr int kColumns = LogitTile::TN;      // token columns per lane
@@ -416,7 +416,7 @@ struct FwdEpilogue {
 // states of the two half-waves and of the two waves sharing a token are merged
 // and written as one partial state per (split, token).
 template <bool CAP, bool FIXED, bool BIAS, bool WSPLIT>
-__global__ void __launch_bounds__(kThreads, 2)
+__global__ void __launch_bounds__(kThreads, kLogitWgsPerCu)
 fwd_stats_kernel(const FwdArgs a) {
   __shared__ __attribute__((aligned(16))) char lds[LogitTile::kLdsBytes];
   const GridPos gp =
@@ -661,7 +661,10 @@ struct DzEpilogue {
     const uint32_t ld_bytes = (uint32_t)a.ldz * 2;
     const __amdgpu_buffer_rsrc_t out =
         tile_rsrc(a.dz + (int64_t)nbase * a.ldz, (int64_t)(a.n - nbase) * ld_bytes);
-    const uint32_t voff = (uint32_t)(lane >> 3) * ld_bytes + (lane & 7) * 16 + (vw - a.c0) * 2;
+    // kRowLanes lanes store one token's kWaveRows values, 16 bytes each
+    constexpr int kRowLanes = kWaveRows * 2 / 16, kPassRows = 64 / kRowLanes;
+    const uint32_t voff = (uint32_t)(lane / kRowLanes) * ld_bytes + (lane % kRowLanes) * 16 +
+                          (vw - a.c0) * 2;
 #pragma unroll
     for (int j = 0; j < kColumns; ++j) {
       float d[kQ];
@@ -712,21 +715,22 @@ struct DzEpilogue {
         }
       }
 #pragma unroll
-      for (int pass = 0; pass < 4; ++pass) {
-        const int tr = pass * 8 + (lane >> 3), c = lane & 7, f = tr >> 1;
+      for (int pass = 0; pass < 32 / kPassRows; ++pass) {
+        const int tr = pass * kPassRows + lane / kRowLanes, c = lane % kRowLanes, f = tr >> 1;
         u32x4 x = *reinterpret_cast<const u32x4*>(buf + tr * (kWaveRows * 2) + ((c ^ (f >> 1)) << 4));
         if (f & 1) x = __builtin_shufflevector(x, x, 2, 3, 0, 1);
         // token nbase + j*32 + tr; tokens past N fall outside the descriptor
         // (the whole offset goes in the lane offset: the scalar offset is not
         // part of the range check)
-        __builtin_amdgcn_raw_buffer_store_b128(x, out, voff + (j * 32 + pass * 8) * ld_bytes, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(x, out, voff + (j * 32 + pass * kPassRows) * ld_bytes,
+                                               0, 0);
       }
     }
   }
 };
 
 template <bool CAP, bool BIAS, bool WSPLIT>
-__global__ void __launch_bounds__(kThreads, 2)
+__global__ void __launch_bounds__(kThreads, kLogitWgsPerCu)
 bwd_dz_kernel(const DzArgs a) {
   __shared__ __attribute__((aligned(16))) char lds[LogitTile::kLdsBytes];
   const int groups = (a.chunk_tiles + a.tiles_per_wg - 1) / a.tiles_per_wg;
