@@ -49,7 +49,62 @@ def parse():
                          "--pmc FETCH_SIZE / WRITE_SIZE output directories of a bench run and of "
                          "a --copy-calibration-mib run (no GPU needed)")
     ap.add_argument("--traffic-kernel", default="contract_kernel")
+    ap.add_argument("--library-gemm", action="store_true",
+                    help="only time the vendor GEMM library (torch.mm, hipBLASLt) on the plain "
+                         "products of the workload's step, as a reference for what a bf16 GEMM "
+                         "of these shapes reaches on this GPU")
     return ap.parse_args()
+
+
+def library_gemm(args) -> int:
+    """Plain bf16 products of one step of the workload through torch.mm
+    (hipBLASLt): the logits (bf16 out), one backward chunk's grad_hidden and
+    grad_weight products, and a square 8192^3 pair for scale.  Each is timed
+    with events over repeated calls after a warmup; nothing here is part of
+    the loss path."""
+    import torch
+
+    from linear_cross_entropy_fp32_amd import synth
+    w = synth.WORKLOADS[args.workload]
+    n, hd, v = w.n_tokens, w.hidden, w.vocab
+    vc = max(128, ((1 << 27) // (2 * n)) // 128 * 128)     # the backward's chunk width
+    vc = min(vc, v)
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device="cpu").manual_seed(0)
+
+    def rnd(*shape):
+        return torch.randn(*shape, generator=g).to(dev).bfloat16()
+
+    wt, h, dz = rnd(v, hd), rnd(n, hd), rnd(n, vc)
+    wc = wt[:vc].contiguous()
+    a8, b8 = rnd(8192, 8192), rnd(8192, 8192)
+    cases = [
+        ("logits lm_head.hidden^T", lambda: torch.mm(wt, h.t()), 2 * v * n * hd),
+        ("logits hidden.lm_head^T", lambda: torch.mm(h, wt.t()), 2 * v * n * hd),
+        ("grad_hidden chunk dz.lm_head", lambda: torch.mm(dz, wc), 2 * n * vc * hd),
+        ("grad_weight chunk dz^T.hidden", lambda: torch.mm(dz.t(), h), 2 * n * vc * hd),
+        ("square 8192 NN", lambda: torch.mm(a8, b8), 2 * 8192 ** 3),
+        ("square 8192 NT", lambda: torch.mm(a8, b8.t()), 2 * 8192 ** 3),
+    ]
+    out = {"workload": w.name, "n_tokens": n, "hidden": hd, "vocab": v, "chunk_rows": vc,
+           "peak_tflops": PEAK_BF16_TFLOPS, "cases": []}
+    for name, fn, flops in cases:
+        for _ in range(5):
+            fn()
+        torch.cuda.synchronize()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 20
+        s.record()
+        for _ in range(reps):
+            fn()
+        e.record()
+        torch.cuda.synchronize()
+        ms = s.elapsed_time(e) / reps
+        tf = flops / (ms * 1e-3) / 1e12
+        out["cases"].append({"product": name, "us": round(ms * 1e3, 1), "tflops": round(tf, 1),
+                             "pct_peak": round(100 * tf / PEAK_BF16_TFLOPS, 1)})
+    print(json.dumps(out), flush=True)
+    return 0
 
 
 def cpu_baseline(w, inp, budget_s: float) -> dict:
@@ -211,6 +266,8 @@ def main() -> int:
         return 2
     import torch
 
+    if args.library_gemm:
+        return library_gemm(args)
     if args.copy_calibration_mib:
         # a plain copy of known size: rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE on
         # this run gives the counters' scale for algorithmic byte counts

@@ -853,7 +853,7 @@ contract_kernel(const ContractArgs a) {
     const Operand opB{a.w, a.hdim, tn * kGemmTileN, a.hdim, a.width};
     GhTile T;
     T.zero();
-    T.run(lds, opA, opB, opB, false, kb, ke);
+    T.run(lds, opA, opB, kb, ke);
     store_tile(T, a.gh + (int64_t)z * a.n * a.hdim, a.hdim, tm * kGemmTileM, tn * kGemmTileN,
                n_rows, a.hdim, a.gh_accumulate != 0);
   } else {
@@ -864,7 +864,7 @@ contract_kernel(const ContractArgs a) {
     const Operand opB{a.h, a.hdim, tn * kGemmTileN, a.hdim, n_rows};
     GwTile T;
     T.zero();
-    T.run(lds, opA, opB, opB, false, 0, n_rows);
+    T.run(lds, opA, opB, 0, n_rows);
     store_tile(T, a.gw, a.hdim, tm * kGemmTileM, tn * kGemmTileN, a.width, a.hdim, false, true);
   }
 }

@@ -7,12 +7,15 @@
 //
 // Operands stream HBM -> LDS in K slices of 32 values through a ring of three
 // LDS stages that buffer loads write directly (buffer_load_dwordx4 ... lds,
-// "LDS DMA"): no staging registers and no LDS store instructions.  Slice kt+2 is issued while
-// slice kt is multiplied, and slice kt is consumed after an explicit
-// "s_waitcnt vmcnt(loads of one slice)" + s_barrier, so only that slice has to
-// have landed (a fenced barrier would make the compiler drain every
-// outstanding load).  Loads return in order, so the wait also holds when the
-// caller's epilogue has issued other memory operations in between.
+// "LDS DMA"): no staging registers and no LDS store instructions.  Two slices
+// are in flight while one is multiplied, and a slice is consumed after an
+// explicit "s_waitcnt vmcnt(loads of one slice)" + s_barrier, so only that
+// slice has to have landed (a fenced barrier would make the compiler drain
+// every outstanding load).  Loads return in order, so the wait also holds
+// when the caller's epilogue has issued other memory operations in between.
+// The streamed loop (run_stream) barriers at the start of each slice; the
+// single-tile loop (run) barriers in the middle of each slice, so that the
+// LDS reads that follow a barrier overlap MFMAs of the same wave.
 // Out-of-range rows and K values read zero through the buffer descriptor
 // bound; no load is branched around.
 //
@@ -49,6 +52,13 @@ typedef short i16x8 __attribute__((ext_vector_type(8)));
 constexpr int kThreads = 256;
 constexpr int kBK = 32;        // K values per slice
 constexpr int kStages = 3;     // LDS ring depth
+// Wave priority (s_setprio) while a tile's K loop runs; epilogues and result
+// stores run at 0.  With two workgroups per CU, a SIMD holds one wave of
+// each: when one is in its VALU-heavy epilogue and the other in its K loop,
+// the arbiter then favours the MFMA and load issue of the K loop.  Measured
+// on the 2048 x 640 x 262144 softcapped workload: -2% per step at 1, less
+// at 2 and 3.
+constexpr int kLoopPriority = 1;
 
 // Row (within a 32x32 block) of accumulator register r of lane l for the
 // 32x32x16 MFMA; the column is l % 32.
@@ -122,6 +132,18 @@ __device__ __forceinline__ void dma16(const u32x4& rs, const char* lds, uint32_t
                "{m0}"(m0));
 }
 
+// Same, with the LDS byte address of the 1 KB block given (wave-uniform).
+__device__ __forceinline__ void dma16_at(const u32x4& rs, uint32_t m0, uint32_t off) {
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(off), "s"(rs),
+               "{m0}"(m0));
+}
+
+// LDS byte address of a pointer into the workgroup's LDS array.
+__device__ __forceinline__ uint32_t lds_addr(const char* p) {
+  return __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p);
+}
+
 // Wait until at most N of this wave's vector memory operations are
 // outstanding, then barrier the workgroup.
 template <int N>
@@ -142,6 +164,12 @@ __device__ __forceinline__ void vm_barrier() {
   else if constexpr (N == 11) asm volatile("s_waitcnt vmcnt(11) lgkmcnt(0)\n\ts_barrier" ::: "memory");
   else asm volatile("s_waitcnt vmcnt(12) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
+
+// s_waitcnt lgkmcnt(0) in a form the compiler sees (vmcnt and expcnt left at
+// their maxima), so that it knows the LDS reads issued so far have completed
+// and places no waits of its own for them later; the waits inside the inline
+// assembly above are invisible to it.
+__device__ __forceinline__ void lds_reads_done() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
 // Workgroup barrier after this wave's LDS accesses have completed; loads
 // into LDS that are still in flight stay in flight.
@@ -185,6 +213,37 @@ struct Stage<R, true> {
       dma16(s.rsrc, lds + blk * 1024, offset_or_oob(gk < s.k_bound, row * s.ld_bytes + gk * 2));
     }
   }
+  // Per-lane load offsets of one tile, computed once: slice k0 adds 2 k0
+  // bytes; a lane's chunk reads zero past the K bound (or when `live` is
+  // false).
+  struct Plan {
+    u32x4 rsrc;
+    uint32_t base[kPerWave];
+    int c8[kPerWave];
+    int k_bound;
+  };
+  __device__ static __forceinline__ Plan plan(const Operand& op) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t rows = (int64_t)op.row_bound - op.row0;
+    Plan pl;
+    pl.rsrc = dma_rsrc(op.ptr + (int64_t)op.row0 * op.ld, rows * op.ld * 2);
+    pl.k_bound = op.k_bound;
+#pragma unroll
+    for (int i = 0; i < kPerWave; ++i) {
+      const int p = (wave * kPerWave + i) * 64 + lane;
+      const int row = p >> 2, c = (p & 3) ^ swz(row);
+      pl.base[i] = (uint32_t)(row * op.ld * 2) + c * 16;
+      pl.c8[i] = c * 8;
+    }
+    return pl;
+  }
+  __device__ static __forceinline__ void issue(const Plan& pl, uint32_t m0, int k0, bool live) {
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+#pragma unroll
+    for (int i = 0; i < kPerWave; ++i)
+      dma16_at(pl.rsrc, m0 + (wave * kPerWave + i) * 1024,
+               offset_or_oob(live && k0 + pl.c8[i] < pl.k_bound, pl.base[i] + k0 * 2));
+  }
   // 8 consecutive K values (from 16 ks + 8 (lane / 32)) of row m0 + lane % 32
   __device__ static __forceinline__ bf16x8 frag(const char* lds, int m0, int ks) {
     const int lane = threadIdx.x & 63;
@@ -223,6 +282,37 @@ struct Stage<R, false> {
       dma16(s.rsrc, lds + blk * 1024,
             offset_or_oob(c * 8 < s.rows, (uint32_t)(k0 + k) * s.ld_bytes + c * 16));
     }
+  }
+  // Per-lane load offsets of one tile, computed once: slice k0 adds k0 K
+  // rows; K rows past the bound fall outside the descriptor, chunks past the
+  // row bound (or every chunk when `live` is false) read zero.
+  struct Plan {
+    u32x4 rsrc;
+    uint32_t base[kPerWave];
+    bool ok[kPerWave];
+    uint32_t ld_bytes;
+  };
+  __device__ static __forceinline__ Plan plan(const Operand& op) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    Plan pl;
+    pl.rsrc = dma_rsrc(op.ptr + op.row0, ((int64_t)op.k_bound * op.ld - op.row0) * 2);
+    pl.ld_bytes = (uint32_t)(op.ld * 2);
+#pragma unroll
+    for (int i = 0; i < kPerWave; ++i) {
+      const int p = (wave * kPerWave + i) * 64 + lane;
+      const int k = p / kCPR, c = (p % kCPR) ^ swz(k);
+      pl.base[i] = (uint32_t)k * pl.ld_bytes + c * 16;
+      pl.ok[i] = c * 8 < op.row_bound - op.row0;
+    }
+    return pl;
+  }
+  __device__ static __forceinline__ void issue(const Plan& pl, uint32_t m0, int k0, bool live) {
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t koff = (uint32_t)k0 * pl.ld_bytes;
+#pragma unroll
+    for (int i = 0; i < kPerWave; ++i)
+      dma16_at(pl.rsrc, m0 + (wave * kPerWave + i) * 1024,
+               offset_or_oob(live && pl.ok[i], pl.base[i] + koff));
   }
   // 8 consecutive K values (from 16 ks + 8 (lane / 32)) of column m0 + lane % 32
   __device__ static __forceinline__ bf16x8 frag(const char* lds, int m0, int ks) {
@@ -292,49 +382,74 @@ struct Tile {
     }
   }
 
-  // Slice `kt` of a one- or two-segment K range [k_begin, k_begin + 32 kt_seg)
-  // into LDS stage `buf`.  Segment 1 (the low half of a split fp32 operand)
-  // reuses A and takes B from b1.  Slices past the end read zero.
-  __device__ __forceinline__ static void issue(char* buf, const typename SA::Src& a,
-                                               const typename SB::Src& b0,
-                                               const typename SB::Src& b1, int kt_seg,
-                                               int k_begin, int kt) {
-    const int seg = kt >= kt_seg ? 1 : 0;
-    const int k0 = k_begin + (kt - seg * kt_seg) * kBK;
-    SA::issue(a, buf, k0);
-    SB::issue(seg ? b1 : b0, buf + kLdsA, k0);
+  // Fragments of K step ks (0 or 1) of the slice held in one LDS stage.
+  __device__ __forceinline__ static void frags(const char* stage, int ks, bf16x8 (&fa)[TM],
+                                               bf16x8 (&fb)[TN]) {
+    const int wave = threadIdx.x >> 6;
+    const int wm = wave & 1, wn = wave >> 1;
+#pragma unroll
+    for (int j = 0; j < TN; ++j) fb[j] = SB::frag(stage + kLdsA, wn * (BN / 2) + j * 32, ks);
+#pragma unroll
+    for (int i = 0; i < TM; ++i) fa[i] = SA::frag(stage, wm * (BM / 2) + i * 32, ks);
+  }
+  __device__ __forceinline__ void mma(const bf16x8 (&fa)[TM], const bf16x8 (&fb)[TN]) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
   }
 
-  // acc = the sum over k in [k_begin, k_end), or twice over it when two_seg
-  // is set (A against b0, then against b1); acc is overwritten (an empty
-  // range leaves it untouched).  The range is read in whole slices:
-  // k_end - k_begin must be a multiple of 32 unless k_end is the operands' K
-  // bound (past which loads read zero).
-  __device__ __forceinline__ void run(char* lds, const Operand a_op, const Operand b0_op,
-                                      const Operand b1_op, bool two_seg, int k_begin, int k_end) {
-    const int kt_seg = (k_end - k_begin + kBK - 1) / kBK;
-    if (kt_seg <= 0) return;
-    const int kt_total = kt_seg * (two_seg ? 2 : 1);
-    const typename SA::Src a = SA::source(a_op);
-    const typename SB::Src b0 = SB::source(b0_op);
-    const typename SB::Src b1 = SB::source(two_seg ? b1_op : b0_op);
-    const int past = 2 * kt_seg;       // a slice index that reads zero in both modes
-    issue(lds, a, b0, b1, kt_seg, k_begin, 0);
-    issue(lds + kStage, a, b0, b1, kt_seg, k_begin, kt_total > 1 ? 1 : past);
-    int slot = 0, nslot = 2;
-    // slice 0 starts the accumulators from zero
-    vm_barrier<kLoads>();
-    issue(lds + nslot * kStage, a, b0, b1, kt_seg, k_begin, kt_total > 2 ? 2 : past);
-    mma_stage<true>(lds);
-    slot = 1;
-    nslot = 0;
-    for (int kt = 1; kt < kt_total; ++kt) {
-      vm_barrier<kLoads>();            // slice kt landed; slice kt-1 no longer read
-      issue(lds + nslot * kStage, a, b0, b1, kt_seg, k_begin, kt + 2 < kt_total ? kt + 2 : past);
-      mma_stage(lds + slot * kStage);
-      slot = slot == kStages - 1 ? 0 : slot + 1;
-      nslot = nslot == kStages - 1 ? 0 : nslot + 1;
+  // acc += the sum over k in [k_begin, k_end), read in whole slices: k_end -
+  // k_begin must be a multiple of 32 unless k_end is the operands' K bound
+  // (past which loads read zero).
+  //
+  // Schedule.  Slice kt lives in stage kt % 3.  The workgroup barrier sits in
+  // the middle of each slice: after the MFMAs of its first K step, a wave
+  // waits until slice kt+1 has landed (loads of one slice may stay in
+  // flight) and until every wave has read slice kt, then refills stage kt % 3
+  // with slice kt+3, reads the first fragments of slice kt+1, and multiplies
+  // the second K step of slice kt meanwhile.  So the LDS reads after a
+  // barrier overlap MFMAs of the same wave, and two slices stay in flight.
+  // Loads past the last slice are issued as zero-reading loads, which keeps
+  // the wait counts the same in every iteration.
+  __device__ __forceinline__ void run(char* lds, const Operand a_op, const Operand b_op,
+                                      int k_begin, int k_end) {
+    const int kt_total = (k_end - k_begin + kBK - 1) / kBK;
+    if (kt_total <= 0) return;
+    const typename SA::Plan a = SA::plan(a_op);
+    const typename SB::Plan b = SB::plan(b_op);
+    const uint32_t l0 = lds_addr(lds);
+    auto issue = [&](int kt, int stage) {
+      const bool live = kt < kt_total;
+      const int k0 = k_begin + (live ? kt : 0) * kBK;
+      const uint32_t m0 = l0 + stage * kStage;
+      SA::issue(a, m0, k0, live);
+      SB::issue(b, m0 + kLdsA, k0, live);
+    };
+    issue(0, 0);
+    issue(1, 1);
+    issue(2, 2);
+    bf16x8 fa0[TM], fb0[TN], fa1[TM], fb1[TN];
+    __builtin_amdgcn_s_setprio(kLoopPriority);
+    vm_barrier<2 * kLoads>();            // slice 0 landed
+    frags(lds, 0, fa0, fb0);
+    int st = 0;                           // stage of slice kt
+    for (int kt = 0; kt < kt_total; ++kt) {
+      const int nst = st == kStages - 1 ? 0 : st + 1;
+      frags(lds + st * kStage, 1, fa1, fb1);
+      mma(fa0, fb0);
+      // keep the compiler from moving these MFMAs past the barrier, where the
+      // wait for the reads above would then stand alone
+      __builtin_amdgcn_sched_barrier(0);
+      lds_reads_done();
+      vm_barrier<kLoads>();              // slice kt+1 landed; slice kt read by every wave
+      issue(kt + 3, st);
+      if (kt + 1 < kt_total) frags(lds + nst * kStage, 0, fa0, fb0);
+      mma(fa1, fb1);
+      st = nst;
     }
+    __builtin_amdgcn_s_setprio(0);
     vm_barrier<0>();
   }
 
@@ -395,6 +510,7 @@ struct Tile {
       // the first slice of a tile starts the accumulators from zero, so they
       // are dead between the previous epilogue and here
       vm_barrier<kLoads>();
+      __builtin_amdgcn_s_setprio(kLoopPriority);
       issue_next();
       mma_stage<true>(lds + cslot * kStage);
       for (int cs = 1; cs < kt_tile; ++cs) {
@@ -403,6 +519,7 @@ struct Tile {
         issue_next();
         mma_stage(lds + cslot * kStage);
       }
+      __builtin_amdgcn_s_setprio(0);   // the epilogue yields issue slots to the other workgroup
       char* free_lds = nullptr;
       if constexpr (Epi::kUsesLds) {
         lds_barrier();                 // every wave is done reading this stage
