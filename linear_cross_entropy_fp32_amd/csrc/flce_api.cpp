@@ -36,12 +36,18 @@ constexpr int64_t kMaxOperandBytes = (int64_t(1) << 31) - 1;
 constexpr size_t kAlign = 256;
 constexpr int64_t kTargetWgs = 2048;                 // forward workgroups: ~8 per CU
 constexpr int64_t kDzWgs = 256 * kLogitWgsPerCu;     // dz workgroups per chunk: one round
+// ... unless that would give a workgroup more vocab tiles than this (at N =
+// 16384 with 16384-row chunks: 8 tiles in two rounds measured 1% faster than
+// 16 in one)
+constexpr int64_t kMaxDzTilesPerWg = 8;
 // bf16 dz of one backward vocab chunk.  A 128 MiB chunk stays in the 256 MB
 // last-level cache (MALL) between the dz write and the contraction's two
 // reads of it; it is used while it leaves the chunk at least kMinChunkWidth
 // vocab rows wide, since narrower chunks unbalance the contraction (few long
 // grad_weight tiles against many short grad_hidden ones).  Otherwise the
-// chunk is 256 MiB.
+// chunk is 256 MiB.  Either way the chunk is at least N rows wide (measured:
+// at N = 16384, 16384-row chunks take 10% off a step at H = 1024 and 5% at
+// H = 4096 against 8192-row ones; at N = 8192, 16384 rows are slower).
 constexpr int64_t kDzChunkBytes = int64_t(1) << 27;
 constexpr int64_t kDzChunkBytesWide = int64_t(1) << 28;
 constexpr int64_t kMinChunkWidth = 8192;
@@ -110,10 +116,17 @@ Plan make_plan(const flce_problem* p) {
   pl.tt_fastest = hidden_bf16_bytes <= kL2Bytes ? 1 : 0;
 
   // backward: vocab chunks of about kDzChunkBytes of bf16 dz, or of
-  // kDzChunkBytesWide when the former would be narrower than kMinChunkWidth
+  // kDzChunkBytesWide when the former would be narrower than kMinChunkWidth;
+  // and at least N rows wide (so a grad_hidden tile's K, the chunk's rows,
+  // is never shorter than a grad_weight tile's K, the N tokens), as long as
+  // the chunk stays below the 2^31-byte operand limit
   int64_t vc = n > 0 ? (kDzChunkBytes / (2 * n)) / kLogitTileV * kLogitTileV : rup(v, kLogitTileV);
   if (n > 0 && vc < kMinChunkWidth)
     vc = (kDzChunkBytesWide / (2 * n)) / kLogitTileV * kLogitTileV;
+  if (n > 0) {
+    vc = std::max<int64_t>(vc, rup(n, kLogitTileV));
+    vc = std::min<int64_t>(vc, kMaxOperandBytes / (2 * n) / kLogitTileV * kLogitTileV);
+  }
   vc = std::min<int64_t>(vc, kMaxOperandBytes / (2 * h) / kLogitTileV * kLogitTileV);
   vc = std::max<int64_t>(vc, kLogitTileV);
   vc = std::min<int64_t>(vc, rup(v, kLogitTileV));
@@ -124,7 +137,8 @@ Plan make_plan(const flce_problem* p) {
   // the workgroups take half as many tiles each: twice as many workgroups,
   // which keeps the GPU filled when a third of the rows carry a loss
   pl.dz_tiles_per_wg = (int)std::max<int64_t>(
-      1, chunk_tiles * pl.n_tok_tiles / kDzWgs / (p->compact_valid ? 2 : 1));
+      1, std::min<int64_t>(kMaxDzTilesPerWg,
+                           chunk_tiles * pl.n_tok_tiles / kDzWgs / (p->compact_valid ? 2 : 1)));
   // grad_hidden split: its workgroups get twice the K depth of the
   // grad_weight ones (N); the launch interleaves the two kinds so every XCD
   // gets the same mix, and fewer splits mean fewer partial slots to update
