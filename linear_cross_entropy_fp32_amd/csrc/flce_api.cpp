@@ -53,6 +53,7 @@ constexpr int64_t kDzChunkBytesWide = int64_t(1) << 28;
 constexpr int64_t kMinChunkWidth = 8192;
 constexpr int64_t kColsumElems = int64_t(1) << 22;   // fp32 partials of the grad_bias sums
 constexpr int64_t kL2Bytes = int64_t(4) << 20;        // L2 of one XCD
+constexpr int64_t kWindowWgs = 64;                    // logit-tile workgroups one XCD holds
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline int64_t rup(int64_t a, int64_t b) { return cdiv(a, b) * b; }
@@ -66,6 +67,7 @@ struct Plan {
   int gh_splits;         // split-K of the grad_hidden contraction
   int64_t gh_kps;
   int cs_segs;           // row segments of the grad_bias column sums
+  int win_tt;            // token tiles per window of the logit-tile order
   int tt_fastest;        // logit-tile workgroup order: token tile fastest when
                          // the bf16 hidden operand fits in one XCD's L2
   size_t off_hsplit, off_part, off_bsums, off_dz, off_ghpart, off_cspart;
@@ -107,13 +109,28 @@ Plan make_plan(const flce_problem* p) {
   const int64_t n = p->n_tokens, h = p->hidden, v = p->vocab;
   pl.n_tok_tiles = (int)cdiv(n, kLogitTileN);
   pl.n_voc_tiles = (int)cdiv(v, kLogitTileV);
-  int64_t splits = n > 0 ? cdiv(kTargetWgs, pl.n_tok_tiles) : 1;
-  splits = std::max<int64_t>(1, std::min<int64_t>(splits, pl.n_voc_tiles));
-  pl.tiles_per_split = (int)cdiv(pl.n_voc_tiles, splits);
-  pl.n_splits = (int)cdiv(pl.n_voc_tiles, pl.tiles_per_split);
   pl.fin_blocks = (int)cdiv(n, kFinalTokens);
   const int64_t hidden_bf16_bytes = n * h * 2 * (p->hidden_dtype == FLCE_F32 ? 2 : 1);
   pl.tt_fastest = hidden_bf16_bytes <= kL2Bytes ? 1 : 0;
+  // token tiles per window of the logit-tile order: 8 when the hidden
+  // operand fits in L2 anyway; else as many as keep their hidden rows within
+  // a quarter of one XCD's L2 (the rest streams lm_head tiles), so that the
+  // workgroups of a window that drift apart still find them there
+  const int64_t tile_bytes = hidden_bf16_bytes / std::max<int64_t>(n, 1) * kLogitTileN;
+  pl.win_tt = 8;
+  if (!pl.tt_fastest) {
+    pl.win_tt = 1;
+    while (pl.win_tt < 8 && 2 * pl.win_tt * tile_bytes <= kL2Bytes / 4) pl.win_tt *= 2;
+  }
+  // forward splits: about kTargetWgs workgroups, and with narrow windows at
+  // least 64 / win_tt splits, so that one window of win_tt token tiles fills
+  // an XCD (fewer splits would put several windows, and their token tiles'
+  // hidden rows, on one XCD at once)
+  int64_t splits = n > 0 ? cdiv(kTargetWgs, pl.n_tok_tiles) : 1;
+  if (!pl.tt_fastest) splits = std::max<int64_t>(splits, kWindowWgs / pl.win_tt);
+  splits = std::max<int64_t>(1, std::min<int64_t>(splits, pl.n_voc_tiles));
+  pl.tiles_per_split = (int)cdiv(pl.n_voc_tiles, splits);
+  pl.n_splits = (int)cdiv(pl.n_voc_tiles, pl.tiles_per_split);
 
   // backward: vocab chunks of about kDzChunkBytes of bf16 dz, or of
   // kDzChunkBytesWide when the former would be narrower than kMinChunkWidth;
@@ -139,6 +156,13 @@ Plan make_plan(const flce_problem* p) {
   pl.dz_tiles_per_wg = (int)std::max<int64_t>(
       1, std::min<int64_t>(kMaxDzTilesPerWg,
                            chunk_tiles * pl.n_tok_tiles / kDzWgs / (p->compact_valid ? 2 : 1)));
+  // with a large hidden operand, fewer tiles per workgroup (more vocabulary
+  // groups per window) until the token tiles an XCD holds at once keep their
+  // hidden rows within half of its L2
+  if (!pl.tt_fastest)
+    while (pl.dz_tiles_per_wg > 1 &&
+           cdiv(kWindowWgs, cdiv(chunk_tiles, pl.dz_tiles_per_wg)) * tile_bytes > kL2Bytes / 2)
+      pl.dz_tiles_per_wg /= 2;
   // grad_hidden split: its workgroups get twice the K depth of the
   // grad_weight ones (N); the launch interleaves the two kinds so every XCD
   // gets the same mix, and fewer splits mean fewer partial slots to update
@@ -385,6 +409,7 @@ int flce_forward(const flce_problem* p, const void* hidden, const void* weight,
     a.n_tok_tiles = pl.n_tok_tiles;
     a.n_splits = pl.n_splits;
     a.tt_fastest = pl.tt_fastest;
+    a.win_tt = pl.win_tt;
     a.tiles_per_split = pl.tiles_per_split;
     a.n_voc_tiles = pl.n_voc_tiles;
     a.part = part;
@@ -481,6 +506,7 @@ int flce_backward(const flce_problem* p, const void* hidden, const void* weight,
   logit_consts(p, d.kx, d.c1, d.c2);
   d.n_tok_tiles = pl.n_tok_tiles;
   d.tt_fastest = pl.tt_fastest;
+  d.win_tt = pl.win_tt;
   d.tiles_per_wg = pl.dz_tiles_per_wg;
   d.dz = dz;
   d.ldz = pl.vc;

@@ -40,6 +40,7 @@ struct FwdArgs {
   float kx, c1, c2;      // see final_u()
   int n_tok_tiles, n_splits, tiles_per_split, n_voc_tiles;
   int tt_fastest;        // workgroup order (see grouped_order)
+  int win_tt;            // token tiles per workgroup window (see grouped_order)
   PartState* part;       // [n_splits, N]
   // row compaction (both null without it): compact row c is row perm[c] of
   // tgt; only rows c < *n_dev are computed (the hidden rows are compacted)
@@ -85,6 +86,7 @@ struct DzArgs {
   int tiles_per_wg;      // vocab tiles streamed by one workgroup
   int n_tok_tiles;
   int tt_fastest;        // workgroup order (see grouped_order)
+  int win_tt;            // token tiles per workgroup window (see grouped_order)
   uint16_t* dz;          // [N, ldz] bf16 chunk buffer
   int64_t ldz;
   // row compaction (both null without it): dz row c belongs to row perm[c] of

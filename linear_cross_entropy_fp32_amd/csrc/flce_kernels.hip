@@ -420,7 +420,8 @@ __global__ void __launch_bounds__(kThreads, kLogitWgsPerCu)
 fwd_stats_kernel(const FwdArgs a) {
   __shared__ __attribute__((aligned(16))) char lds[LogitTile::kLdsBytes];
   const GridPos gp =
-      grouped_order(xcd_remap(blockIdx.x, gridDim.x), a.n_tok_tiles, a.n_splits, a.tt_fastest);
+      grouped_order(xcd_remap(blockIdx.x, gridDim.x), a.n_tok_tiles, a.n_splits, a.win_tt,
+                    a.tt_fastest);
   const int tt = gp.tt, sp = gp.grp;
   const int n0 = tt * kLogitTileN;
   const int n_rows = a.n_dev ? *a.n_dev : a.n;   // rows computed (compacted rows first)
@@ -735,7 +736,8 @@ bwd_dz_kernel(const DzArgs a) {
   __shared__ __attribute__((aligned(16))) char lds[LogitTile::kLdsBytes];
   const int groups = (a.chunk_tiles + a.tiles_per_wg - 1) / a.tiles_per_wg;
   const GridPos gp =
-      grouped_order(xcd_remap(blockIdx.x, gridDim.x), a.n_tok_tiles, groups, a.tt_fastest);
+      grouped_order(xcd_remap(blockIdx.x, gridDim.x), a.n_tok_tiles, groups, a.win_tt,
+                    a.tt_fastest);
   const int tt = gp.tt, grp = gp.grp;
   const int n0 = tt * kLogitTileN;
   const int n_rows = a.n_dev ? *a.n_dev : a.n;   // rows computed (compacted rows first)
