@@ -54,6 +54,10 @@ SMALL = [
     synth.small_workload(260, 136, 1900, 28, weight_dtype="f32", hidden_dtype="f32",
                          reduction="none"),
     synth.small_workload(4100, 64, 30000, 29, weight_dtype="f32", logit_scale=2.0),
+    # hidden operands past one XCD's L2 (4 MB as bf16): windows of one token
+    # tile, at least 64 forward splits, and (fp32) one dz tile per workgroup
+    synth.small_workload(600, 4096, 9000, 41, softcap=30.0, bias=True),
+    synth.small_workload(2000, 4096, 16500, 42, hidden_dtype="f32", reduction="none"),
 ]
 
 
