@@ -40,6 +40,7 @@ constexpr int64_t kDzWgs = 256 * kLogitWgsPerCu;     // dz workgroups per chunk:
 // 16384 with 16384-row chunks: 8 tiles in two rounds measured 1% faster than
 // 16 in one)
 constexpr int64_t kMaxDzTilesPerWg = 8;
+constexpr int64_t kMaxGhSplits = 32;                  // grad_hidden split-K slots
 // bf16 dz of one backward vocab chunk.  A 128 MiB chunk stays in the 256 MB
 // last-level cache (MALL) between the dz write and the contraction's two
 // reads of it; it is used while it leaves the chunk at least kMinChunkWidth
@@ -164,11 +165,14 @@ Plan make_plan(const flce_problem* p) {
            cdiv(kWindowWgs, cdiv(chunk_tiles, pl.dz_tiles_per_wg)) * tile_bytes > kL2Bytes / 2)
       pl.dz_tiles_per_wg /= 2;
   // grad_hidden split: its workgroups get twice the K depth of the
-  // grad_weight ones (N); the launch interleaves the two kinds so every XCD
-  // gets the same mix, and fewer splits mean fewer partial slots to update
+  // grad_weight ones (N), but at least 1024; the launch interleaves the two
+  // kinds so every XCD gets the same mix, and fewer splits mean fewer partial
+  // slots to update.  At most kMaxGhSplits (only small N reaches it: at
+  // N = 256, V = 32000, 32 splits of K = 1000 take a step from 91 to 83 us
+  // against 16; 64 cost more in the final sum over the slots)
   const int64_t width = std::min<int64_t>(vc, v);
   int64_t ghs = n > 0 ? cdiv(width, std::max<int64_t>(2 * n, 1024)) : 1;
-  ghs = std::max<int64_t>(1, std::min<int64_t>(ghs, 16));
+  ghs = std::max<int64_t>(1, std::min<int64_t>(ghs, kMaxGhSplits));
   pl.gh_kps = rup(cdiv(width, ghs), kSliceK);
   pl.gh_splits = (int)cdiv(width, pl.gh_kps);
 
