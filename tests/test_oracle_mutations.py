@@ -20,6 +20,7 @@ PIN_TESTS = [
     (pins.test_gradient_identities, {}),
     (pins.test_num_items_divisor, {}),
     (pins.test_bad_targets_are_counted_and_ignored, {}),
+    (pins.test_margin_against_topk, {}),
 ]
 
 
@@ -101,6 +102,25 @@ def _forward_last_argmax(hidden, weight, bias, targets, prob, rows=None):
     return f
 
 
+def _forward_margin_zero(*a, **k):
+    f = orc_forward_orig(*a, **k)
+    f["margin"] = np.zeros_like(f["margin"])
+    return f
+
+
+def _forward_margin_top1_minus_top3(hidden, weight, bias, targets, prob, rows=None):
+    f = orc_forward_orig(hidden, weight, bias, targets, prob, rows)
+    h = np.asarray(hidden, dtype=np.float64)
+    if rows is not None:
+        h = h[rows]
+    z = orc.final_logits(h, np.asarray(weight, dtype=np.float64), bias, prob)
+    v = z.shape[1]
+    if v >= 3:
+        top = np.sort(z, axis=1)
+        f["margin"] = top[:, -1] - top[:, -3]
+    return f
+
+
 orc_forward_orig = orc.forward
 
 MUTATIONS = {
@@ -114,6 +134,8 @@ MUTATIONS = {
     "bad_targets_not_counted": ("valid_mask", _valid_counts_bad_targets),
     "entropy_sign": ("forward", _forward_entropy_sign),
     "argmax_highest_index": ("forward", _forward_last_argmax),
+    "margin_zero": ("forward", _forward_margin_zero),
+    "margin_top1_minus_top3": ("forward", _forward_margin_top1_minus_top3),
 }
 
 

@@ -338,3 +338,87 @@ def test_bad_targets_are_counted_and_ignored():
     f = forward(hid, w, b, t, Problem())
     assert f["n_bad"] == 2 and f["n_valid"] == 4
     assert f["loss"][2] == 0 and f["loss"][4] == 0
+
+
+# ------------------------------------------------------------- top-2 margin
+
+def _torch_final_logits(hid, w, b, prob):
+    """Final logits through torch float64 (an independent code path)."""
+    h_t = torch.tensor(hid, dtype=torch.float64)
+    w_t = torch.tensor(w, dtype=torch.float64)
+    b_t = None if b is None else torch.tensor(b, dtype=torch.float64)
+    z = torch.nn.functional.linear(h_t, w_t, b_t) * prob.logit_scale
+    if prob.softcap > 0:
+        z = torch.tanh(z / prob.softcap) * prob.softcap
+    return z
+
+
+def _topk_margin(z):
+    if z.shape[1] == 1:
+        return np.full(z.shape[0], np.inf)
+    top = torch.topk(z, 2, dim=1).values
+    return (top[:, 0] - top[:, 1]).numpy()
+
+
+def test_margin_against_topk():
+    """The top-2 margin that decides which rows get argmax / hit parity is
+    top-1 minus top-2 of the final logits (argmax is taken on the final
+    logits: cce pull request, review "Correctness"), checked against
+    torch.topk in float64: random rows, exact ties (two identical lm_head
+    rows, so the margin is exactly 0 on every row where they lead, and the
+    argmax is the lower of the two), V = 2 (|z0 - z1|) and V = 1 (inf)."""
+    hid, w, b, t = _rand_problem(40, 6, 29, 101)
+    prob = Problem(logit_scale=0.8, softcap=4.0)
+    f = forward(hid, w, b, t, prob)
+    z = _torch_final_logits(hid, w, b, prob)
+    assert np.allclose(f["margin"], _topk_margin(z), atol=1e-13)
+    assert np.all(f["margin"] > 0)
+
+    # ties: rows 3 and 17 of W and of the bias are equal, and the bias makes
+    # them lead on every row
+    w2 = w.copy()
+    w2[17] = w2[3]
+    b2 = b.copy()
+    b2[17] = b2[3] = 50.0
+    f2 = forward(hid, w2, b2, t, Problem())
+    z2 = _torch_final_logits(hid, w2, b2, Problem())
+    lead = torch.argmax(z2, dim=1).numpy()
+    assert np.all(lead == 3) and np.all(f2["argmax"] == 3)
+    assert np.all(f2["margin"] == 0.0)
+    assert np.array_equal(f2["margin"], _topk_margin(z2))
+
+    w3 = w[:2]
+    f3 = forward(hid, w3, None, np.zeros(40, dtype=np.int64), Problem())
+    z3 = hid @ w3.T
+    assert np.allclose(f3["margin"], np.abs(z3[:, 0] - z3[:, 1]), atol=1e-13)
+
+    f4 = forward(hid, w[:1], None, np.zeros(40, dtype=np.int64), Problem())
+    assert np.all(np.isinf(f4["margin"]))
+
+
+def test_many_row_blocks_against_torch():
+    """N * V > 3 * 2^24, so the oracle materialises its logits in four row
+    blocks (the path every full-size workload takes): per-token loss, lse,
+    entropy, argmax and margin against torch float64 (linear + cross_entropy
+    + logsumexp + Categorical entropy + topk) on every row, ragged V."""
+    n, h, v = 600, 8, 100003
+    rng = np.random.default_rng(111)
+    hid = rng.standard_normal((n, h))
+    w = rng.standard_normal((v, h)) * 0.3
+    b = rng.standard_normal(v) * 0.1
+    t = rng.integers(0, v, n)
+    t[::17] = IGNORE_INDEX
+    prob = Problem(logit_scale=1.5)
+    f = forward(hid, w, b, t, prob)
+    z = _torch_final_logits(hid, w, b, prob)
+    tt = torch.tensor(t)
+    loss = torch.nn.functional.cross_entropy(z, tt, ignore_index=IGNORE_INDEX,
+                                             reduction="none").numpy()
+    valid = t != IGNORE_INDEX
+    assert np.allclose(f["loss"], loss, atol=1e-11)
+    assert np.allclose(f["lse"], torch.logsumexp(z, dim=1).numpy(), atol=1e-11)
+    ent = torch.distributions.Categorical(logits=z).entropy().numpy()
+    assert np.allclose(f["entropy"][valid], ent[valid], atol=1e-10)
+    assert np.array_equal(f["argmax"], torch.argmax(z, dim=1).numpy())
+    assert np.allclose(f["margin"], _topk_margin(z), atol=1e-12)
+    assert math.isclose(f["loss_mean"], float(loss[valid].mean()), rel_tol=1e-12)
