@@ -86,14 +86,36 @@ typedef struct flce_problem {
                             modes up to summation order.                        */
 } flce_problem;
 
-/* Check the problem description only (no HIP call).  0 or FLCE_ERR_*. */
+/* Check the problem description only (no HIP call).  0 or FLCE_ERR_*.
+ * Defined by: the first TRL page's review, "Correctness" preamble (the fused
+ * kernel refuses mismatched operand dtypes) and the Liger-Kernel page,
+ * "Summary" (unsupported options are refused up front): an unsupported dtype,
+ * shape or scalar is an error code here, before any work is queued.
+ * H must be a multiple of 8 (one 16-byte bf16 load covers 8 hidden values and
+ * every row starts 16-byte aligned); N*H*2 and V*H*2 bytes stay below 2^31 so
+ * that one buffer descriptor addresses each operand.  A larger batch is split
+ * by the caller: the loss is a sum over rows (reduction "sum", or "mean" with
+ * mean_divisor = the total number of valid rows). */
 int flce_validate(const flce_problem* p);
 
 /* Bytes of device workspace one forward or backward call needs (the same
- * buffer serves both).  Returns 0 and sets *bytes on success. */
+ * buffer serves both).  Returns 0 and sets *bytes (host memory) on success;
+ * FLCE_ERR_NULL for a null bytes, else flce_validate's code.  The workspace
+ * holds partial states and at most one backward vocabulary chunk of dz, never
+ * the (tokens x vocab) logits: the first TRL page's opening description (the
+ * loss of hidden @ lm_head.T without materialising the logit matrix). */
 int flce_workspace_bytes(const flce_problem* p, size_t* bytes);
 
-/* Forward.
+/* Forward: per-token loss, lse, entropy, argmax and hit, and the reductions.
+ * Defined by the first TRL page ("Add loss_type="cce", a fused linear
+ * cross-entropy loaded from the Hub"): "What it supports" (bias, logit_scale,
+ * fp32 hidden states, final_logit_softcapping; entropy and token accuracy from
+ * the same fused pass; the helper's 4-tuple) and the review's "Correctness"
+ * preamble (product in the compute dtype with fp32 accumulation, then + bias
+ * in fp32, then * logit_scale, then softcap; entropy = lse - sum p z; argmax
+ * on the final logits), with item 2 (ignored rows still projected unless
+ * compact_valid is set; validity zeroes their weight) and item 5 (an
+ * all-ignored batch gives a zero loss).
  *   hidden   [N, H]  bf16 or fp32 (per p->hidden_dtype), 16-byte aligned
  *   weight   [V, H]  bf16 or fp32 (per p->weight_dtype), 16-byte aligned
  *   bias     [V]     fp32, or NULL for no bias
@@ -111,7 +133,16 @@ int flce_forward(const flce_problem* p, const void* hidden, const void* weight,
                  float* entropy, uint8_t* hit, int32_t* argmax, float* reduced_f32,
                  int64_t* reduced_i64, void* workspace, size_t workspace_bytes, void* stream);
 
-/* Backward of the reduced loss.
+/* Backward of the reduced loss: grad_hidden, grad_weight, grad_bias.
+ * Defined by the first TRL page's review, "Correctness" item 2 (the backward
+ * recomputes the softmax gradient d for the rows and contracts it with the
+ * lm_head and the hidden states) and item 5 (an all-ignored batch still
+ * produces exactly-zero gradients for every parameter), and by the Liger-Kernel
+ * page, "Summary" item 2 (the per-row upstream gradient of reduction "none" is
+ * one fp32 multiply per row, with no device-to-host sync and no BT x V
+ * temporary).  dz is formed in fp32 and rounded to bf16 for the MFMA
+ * contractions, one vocabulary chunk at a time (see flce_plan_info).
+ * Ownership and errors as for flce_forward.
  *   lse [N] and reduced_i64 [3] are the forward's outputs for the same inputs
  *   (n_valid is read on the device for FLCE_GRAD_MEAN; no host sync).
  *   grad_mode: FLCE_GRAD_MEAN / FLCE_GRAD_SUM read grad_out[0];
@@ -125,7 +156,9 @@ int flce_backward(const flce_problem* p, const void* hidden, const void* weight,
                   float* grad_hidden, float* grad_weight, float* grad_bias, void* workspace,
                   size_t workspace_bytes, void* stream);
 
-/* Benchmark instrumentation (not part of the loss API).  While set, every
+/* Benchmark instrumentation (support, not part of the loss API; it measures
+ * the kernels as the Liger-Kernel page's "Details" times them: events around
+ * the launches on the caller's stream).  While set, every
  * launch of `kernel` made by this thread is bracketed by hipEventRecord of
  * events[2i] before and events[2i+1] after it, on the launch stream, for
  * i = 0 .. n_pairs-1; later launches are not recorded.  `events` holds
@@ -137,6 +170,25 @@ int flce_backward(const flce_problem* p, const void* hidden, const void* weight,
 #define FLCE_KERNEL_BWD_DZ 1
 #define FLCE_KERNEL_CONTRACT 2
 int flce_set_timing_events(int kernel, void* const* events, int n_pairs);
+
+/* How the library tiles a problem (support; nothing is launched, no HIP
+ * call).  Writes min(n_out, FLCE_PLAN_FIELDS) values to out (host memory), in
+ * this order, and returns that count, or a negative FLCE_ERR_* code for an
+ * invalid problem or a null out:
+ *   0 chunk_rows       vocabulary rows per backward chunk (Vc, a multiple of 128)
+ *   1 n_chunks         backward chunks (contraction launches per backward)
+ *   2 fwd_splits       vocabulary splits of the forward statistics
+ *   3 fwd_tiles_per_split  128-row vocabulary tiles per forward split
+ *   4 dz_tiles_per_wg  vocabulary tiles per workgroup of the dz recompute
+ *   5 gh_splits        grad_hidden split-K slots per chunk
+ *   6 gh_rows_per_split  vocabulary rows per slot (a multiple of 32)
+ *   7 window_token_tiles  token tiles per 64-workgroup window of the logit order
+ *   8 token_tile_fastest  1: windows take the token tile fastest
+ *   9 fwd_workspace_bytes, 10 bwd_workspace_bytes, 11 workspace_bytes
+ *  12 dz_chunk_bytes   N * chunk_rows * 2 (the largest (tokens x vocab) buffer)
+ */
+#define FLCE_PLAN_FIELDS 13
+int flce_plan_info(const flce_problem* p, int64_t* out, int n_out);
 
 /* Description of the last error on this thread ("" if none). */
 const char* flce_last_error(void);

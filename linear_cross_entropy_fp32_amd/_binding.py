@@ -22,7 +22,11 @@ ERROR_NAMES = {-1: "FLCE_ERR_NULL", -2: "FLCE_ERR_SHAPE", -3: "FLCE_ERR_DTYPE",
                -4: "FLCE_ERR_ALIGN", -5: "FLCE_ERR_WORKSPACE", -6: "FLCE_ERR_HIP",
                -7: "FLCE_ERR_ARG"}
 EXPORTED = ("flce_validate", "flce_workspace_bytes", "flce_forward", "flce_backward",
-            "flce_last_error", "flce_abi_version", "flce_set_timing_events")
+            "flce_last_error", "flce_abi_version", "flce_set_timing_events", "flce_plan_info")
+PLAN_FIELDS = ("chunk_rows", "n_chunks", "fwd_splits", "fwd_tiles_per_split",
+               "dz_tiles_per_wg", "gh_splits", "gh_rows_per_split", "window_token_tiles",
+               "token_tile_fastest", "fwd_workspace_bytes", "bwd_workspace_bytes",
+               "workspace_bytes", "dz_chunk_bytes")
 FLCE_KERNEL_FWD_STATS, FLCE_KERNEL_BWD_DZ, FLCE_KERNEL_CONTRACT = 0, 1, 2
 
 
@@ -70,6 +74,8 @@ def lib() -> ctypes.CDLL:
         L.flce_abi_version.restype = ctypes.c_int
         L.flce_set_timing_events.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_int]
         L.flce_set_timing_events.restype = ctypes.c_int
+        L.flce_plan_info.argtypes = [pp, ctypes.POINTER(ctypes.c_int64), ctypes.c_int]
+        L.flce_plan_info.restype = ctypes.c_int
         if L.flce_abi_version() != 1:
             raise RuntimeError("libflce.so ABI version mismatch: rebuild it")
         _lib = L
@@ -98,6 +104,15 @@ def flce_workspace_bytes(prob: FlceProblem) -> int:
     out = ctypes.c_size_t(0)
     _check(lib().flce_workspace_bytes(ctypes.byref(prob), ctypes.byref(out)))
     return out.value
+
+
+def flce_plan_info(prob: FlceProblem) -> dict:
+    """``flce_plan_info``: how the library tiles the problem (host only)."""
+    out = (ctypes.c_int64 * len(PLAN_FIELDS))()
+    rc = lib().flce_plan_info(ctypes.byref(prob), out, len(PLAN_FIELDS))
+    if rc < 0:
+        raise FlceError(rc, flce_last_error())
+    return dict(zip(PLAN_FIELDS, (int(x) for x in out[:rc])))
 
 
 def flce_last_error() -> str:

@@ -52,6 +52,12 @@ constexpr int64_t kMaxGhSplits = 32;                  // grad_hidden split-K slo
 constexpr int64_t kDzChunkBytes = int64_t(1) << 27;
 constexpr int64_t kDzChunkBytesWide = int64_t(1) << 28;
 constexpr int64_t kMinChunkWidth = 8192;
+// At most this many vocabulary rows per backward chunk.  The kernels form
+// buffer offsets in 32 bits: a dz row of the chunk is 2 * Vc bytes, and a
+// tile reaches up to 256 rows past its base (phantom token rows past N
+// included), so 256 * 2 * Vc must stay well below 2^31 (here 2^30).  Only tiny
+// N reaches the cap: otherwise the 2^27..2^28-byte chunk rule is narrower.
+constexpr int64_t kMaxChunkRows = int64_t(1) << 21;
 constexpr int64_t kColsumElems = int64_t(1) << 22;   // fp32 partials of the grad_bias sums
 constexpr int64_t kL2Bytes = int64_t(4) << 20;        // L2 of one XCD
 constexpr int64_t kWindowWgs = 64;                    // logit-tile workgroups one XCD holds
@@ -146,6 +152,7 @@ Plan make_plan(const flce_problem* p) {
     vc = std::min<int64_t>(vc, kMaxOperandBytes / (2 * n) / kLogitTileV * kLogitTileV);
   }
   vc = std::min<int64_t>(vc, kMaxOperandBytes / (2 * h) / kLogitTileV * kLogitTileV);
+  vc = std::min<int64_t>(vc, kMaxChunkRows);
   vc = std::max<int64_t>(vc, kLogitTileV);
   vc = std::min<int64_t>(vc, rup(v, kLogitTileV));
   pl.vc = vc;
@@ -351,6 +358,22 @@ int flce_set_timing_events(int kernel, void* const* events, int n_pairs) {
 }
 
 const char* flce_last_error(void) { return g_err; }
+
+int flce_plan_info(const flce_problem* p, int64_t* out, int n_out) {
+  g_err[0] = 0;
+  if (!out) return fail(FLCE_ERR_NULL, "out is NULL");
+  if (n_out < 0) return fail(FLCE_ERR_ARG, "n_out must be >= 0");
+  const int rc = validate(p);
+  if (rc) return rc;
+  const Plan pl = make_plan(p);
+  const int64_t v[FLCE_PLAN_FIELDS] = {
+      pl.vc, pl.n_chunks, pl.n_splits, pl.tiles_per_split, pl.dz_tiles_per_wg, pl.gh_splits,
+      pl.gh_kps, pl.win_tt, pl.tt_fastest, (int64_t)pl.fwd_bytes, (int64_t)pl.bwd_bytes,
+      (int64_t)pl.bytes, p->n_tokens * pl.vc * 2};
+  const int k = n_out < FLCE_PLAN_FIELDS ? n_out : FLCE_PLAN_FIELDS;
+  for (int i = 0; i < k; ++i) out[i] = v[i];
+  return k;
+}
 
 int flce_validate(const flce_problem* p) {
   g_err[0] = 0;
