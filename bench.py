@@ -6,6 +6,14 @@ One step = flce_forward + flce_backward (the whole hot path) over one batch of
 seeded synthetic inputs already resident in HBM.  The default workload is the
 262144-vocabulary / hidden-640 / 2048-token batch with softcap 30 (the
 configuration the metric is quoted on).  Prints one JSON line.
+
+Timing protocol (after the Liger-Kernel page's "Details", a do_bench-style
+loop): one discarded call, warmup of at least W steps and 25 ms, then K timed
+steps, each preceded by a 512 MiB write that evicts L2 and the 256 MB MALL
+(outside the step's own event bracket); `value` and `ms_per_step` are the
+median of those flushed steps.  The same K steps back to back (caches warm)
+are reported beside them.  `per_config` repeats the measurement, with fewer
+steps, on the other workloads of the metric.
 """
 from __future__ import annotations
 
@@ -31,9 +39,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--cold-steps", type=int, default=10,
-                    help="after the timed steps, this many steps each preceded (outside their "
-                         "event bracket) by a 512 MiB write that evicts L2 and MALL; 0 = none")
+    ap.add_argument("--per-config-steps", type=int, default=5,
+                    help="timed steps per workload of the per_config record; 0 = no per_config")
     ap.add_argument("--workload", default="huge_vocab")
     ap.add_argument("--compact", action="store_true",
                     help="valid-row compaction (flce_problem.compact_valid): only the rows that "
@@ -41,6 +48,7 @@ def parse():
                          "the flop figures count the valid rows")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--per-config-cpu-seconds", type=float, default=3.0)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (HBM counter scale)")
     ap.add_argument("--traffic-record", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR",
@@ -134,8 +142,20 @@ def cpu_baseline(w, inp, budget_s: float) -> dict:
         rows = sl.stop
     dt = time.perf_counter() - t0
     return {"value": rows / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "cpu_model": _cpu_model(), "nproc": len(os.sched_getaffinity(0)),
             "sample": f"first {rows} of {w.n_tokens} tokens in 128-token batches, fwd+bwd "
                       f"(float64 numpy), {dt:.1f} s"}
+
+
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 # Timing-only events: no system-scope fence (cache writeback and invalidate)
@@ -256,6 +276,204 @@ def write_traffic_record(args) -> int:
     return 0
 
 
+PER_CONFIG = ("tiny", "huge_vocab", "bias_none", "zipf_sum", "fp32_hidden",
+              "fp32_hidden_all_ignored")
+WARMUP_MS = 25.0
+FLUSH_BYTES = 512 << 20
+
+
+class Runner:
+    """One workload's inputs, outputs and workspace resident on the GPU, and
+    the two calls of a step through the C ABI on the current stream."""
+
+    def __init__(self, w, compact: bool):
+        import torch
+
+        import linear_cross_entropy_fp32_amd as flce
+        from linear_cross_entropy_fp32_amd import _binding, synth
+        self.w = w
+        dev = torch.device("cuda:0")
+        self.inp = inp = synth.make_inputs(w)
+        self.h = inp.hidden.to(dev)
+        self.wt = inp.weight.to(dev)
+        self.b = None if inp.bias is None else inp.bias.to(dev)
+        self.t = inp.targets.to(dev)
+        self.go = inp.grad_out.to(dev).reshape(-1)
+        n, hd, v = w.n_tokens, w.hidden, w.vocab
+        self.prob = _binding.problem_for(self.h, self.wt, w.logit_scale, w.softcap,
+                                         compact_valid=compact)
+        self.ws_bytes = flce.flce_workspace_bytes(self.prob)
+        self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=dev)
+        f32 = dict(dtype=torch.float32, device=dev)
+        self.loss, self.lse, self.ent = (torch.empty(n, **f32) for _ in range(3))
+        self.hit = torch.empty(n, dtype=torch.uint8, device=dev)
+        self.red_f = torch.empty(3, **f32)
+        self.red_i = torch.empty(3, dtype=torch.int64, device=dev)
+        self.gh = torch.empty(n, hd, **f32)
+        self.gw = torch.empty(v, hd, **f32)
+        self.gb = torch.empty(v, **f32) if self.b is not None else None
+        self.mode = {"mean": 0, "sum": 1, "none": 2}[w.reduction]
+        self.L = flce.lib()
+        self.P = _binding._ptr
+        self.flce = flce
+        self.stream = torch.cuda.current_stream(dev)
+        self.sp = ctypes.c_void_p(self.stream.cuda_stream)
+
+    def fwd(self):
+        P = self.P
+        rc = self.L.flce_forward(ctypes.byref(self.prob), P(self.h), P(self.wt), P(self.b),
+                                 P(self.t), P(self.loss), P(self.lse), P(self.ent), P(self.hit),
+                                 None, P(self.red_f), P(self.red_i), P(self.ws), self.ws_bytes,
+                                 self.sp)
+        if rc:
+            raise self.flce.FlceError(rc, self.flce.flce_last_error())
+
+    def bwd(self):
+        P = self.P
+        rc = self.L.flce_backward(ctypes.byref(self.prob), P(self.h), P(self.wt), P(self.b),
+                                  P(self.t), P(self.lse), P(self.red_i), self.mode, P(self.go),
+                                  P(self.gh), P(self.gw), P(self.gb), P(self.ws), self.ws_bytes,
+                                  self.sp)
+        if rc:
+            raise self.flce.FlceError(rc, self.flce.flce_last_error())
+
+
+class Events:
+    """Timing-only HIP events (no system-scope fence when recorded)."""
+
+    def __init__(self, hip, count: int):
+        self.hip = hip
+        self.arr = (ctypes.c_void_p * max(1, count))()
+        for i in range(count):
+            _hip_ok(hip.hipEventCreateWithFlags(
+                ctypes.byref(self.arr, i * ctypes.sizeof(ctypes.c_void_p)), _EVENT_TIMING_ONLY))
+        self.count = count
+
+    def __getitem__(self, i):
+        return self.arr[i]
+
+    def ms(self, a, b) -> float:
+        out = ctypes.c_float(0.0)
+        _hip_ok(self.hip.hipEventElapsedTime(ctypes.byref(out), ctypes.c_void_p(self.arr[a]),
+                                             ctypes.c_void_p(self.arr[b])))
+        return out.value
+
+    def close(self):
+        for i in range(self.count):
+            self.hip.hipEventDestroy(ctypes.c_void_p(self.arr[i]))
+
+
+def measure(r: Runner, steps: int, warmup: int, hip, kernel_events: bool) -> dict:
+    """Warm up, then time `steps` flushed steps and `steps` back-to-back ones.
+    Returns per-step times, the forward / backward split of the flushed
+    steps and, with kernel_events, the contraction launches' durations in
+    the flushed steps (recorded by the library on the launch stream)."""
+    import torch
+
+    from linear_cross_entropy_fp32_amd import _binding
+    sp = r.sp
+
+    def mark(e):
+        _hip_ok(hip.hipEventRecord(ctypes.c_void_p(e), sp))
+
+    # one discarded call, then at least `warmup` steps and WARMUP_MS
+    r.fwd()
+    r.bwd()
+    torch.cuda.synchronize()
+    t0, done = time.perf_counter(), 0
+    while done < warmup or (time.perf_counter() - t0) * 1e3 < WARMUP_MS:
+        r.fwd()
+        r.bwd()
+        done += 1
+        if done % 4 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    warm_ms_total = (time.perf_counter() - t0) * 1e3
+
+    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda:0")
+    ev = Events(hip, 3 * steps + 2 * steps)
+    n_pairs = steps * _chunks_per_backward(r.prob) + 1 if kernel_events else 0
+    kev = Events(hip, 2 * n_pairs) if kernel_events else None
+    if kernel_events:
+        r.flce.flce_set_timing_events(_binding.FLCE_KERNEL_CONTRACT, kev.arr, n_pairs)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    for i in range(steps):
+        flush.fill_(i & 255)
+        mark(ev[3 * i])
+        r.fwd()
+        mark(ev[3 * i + 1])
+        r.bwd()
+        mark(ev[3 * i + 2])
+    torch.cuda.synchronize()
+    wall_cold = time.perf_counter() - t_wall
+    kern_ms = []
+    if kernel_events:
+        recorded = r.flce.flce_set_timing_events(_binding.FLCE_KERNEL_CONTRACT, None, 0)
+        if recorded >= n_pairs:
+            raise RuntimeError("more contraction launches than timing events")
+        kern_ms = [kev.ms(2 * i, 2 * i + 1) for i in range(recorded)]
+        kev.close()
+    # the same steps back to back, caches warm
+    base = 3 * steps
+    for i in range(steps):
+        mark(ev[base + 2 * i])
+        r.fwd()
+        r.bwd()
+        mark(ev[base + 2 * i + 1])
+    torch.cuda.synchronize()
+    cold = [ev.ms(3 * i, 3 * i + 2) for i in range(steps)]
+    fwd = [ev.ms(3 * i, 3 * i + 1) for i in range(steps)]
+    bwd = [ev.ms(3 * i + 1, 3 * i + 2) for i in range(steps)]
+    warm = [ev.ms(base + 2 * i, base + 2 * i + 1) for i in range(steps)]
+    ev.close()
+    del flush
+    return {"cold": cold, "fwd": fwd, "bwd": bwd, "warm": warm, "kern_ms": kern_ms,
+            "warmup_steps": done + 1, "warmup_ms": warm_ms_total, "wall_s": wall_cold}
+
+
+def pct(xs, q):
+    return float(np.percentile(xs, q))
+
+
+def per_config(args, hip) -> dict:
+    """Every workload of the metric, fewer steps each: ms/step (median of the
+    flushed steps), tokens/s, TFLOP/s and % of the bf16 peak (8NHV), the
+    forward / backward split, and the oracle's tokens/s on a bounded sample."""
+    import gc
+
+    import torch
+
+    from linear_cross_entropy_fp32_amd import synth
+    out = {}
+    for name in PER_CONFIG:
+        w = synth.WORKLOADS[name]
+        r = Runner(w, compact=False)
+        m = measure(r, args.per_config_steps, 3, hip, kernel_events=False)
+        ms = pct(m["cold"], 50)
+        flops = 8.0 * w.n_tokens * w.hidden * w.vocab
+        rec = {"n_tokens": w.n_tokens, "hidden": w.hidden, "vocab": w.vocab,
+               "hidden_dtype": w.hidden_dtype, "bias": w.bias, "logit_scale": w.logit_scale,
+               "softcap": w.softcap, "targets": w.targets, "reduction": w.reduction,
+               "ms_per_step": ms, "ms_p20_p80": [pct(m["cold"], 20), pct(m["cold"], 80)],
+               "warm_ms_per_step": pct(m["warm"], 50),
+               "tokens_per_s": w.n_tokens / (ms * 1e-3),
+               "tflops": flops / (ms * 1e-3) / 1e12,
+               "pct_bf16_peak": 100.0 * flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+               "fwd_ms": pct(m["fwd"], 50), "bwd_ms": pct(m["bwd"], 50),
+               "n_valid": int(r.red_i[0].item())}
+        if not args.no_cpu_baseline and w.targets != "all_ignored":
+            cb = cpu_baseline(w, r.inp, args.per_config_cpu_seconds)
+            rec["cpu_oracle_tokens_per_s"] = cb["value"]
+            rec["gpu_speedup_vs_cpu_oracle"] = rec["tokens_per_s"] / cb["value"]
+        out[name] = rec
+        print(f"bench.py: per_config {name}: {ms:.3f} ms/step", file=sys.stderr, flush=True)
+        del r
+        gc.collect()
+        torch.cuda.empty_cache()
+    return out
+
+
 def main() -> int:
     args = parse()
     if args.traffic_record:
@@ -280,155 +498,57 @@ def main() -> int:
         print(json.dumps({"copy_calibration_bytes": n, "copies": max(1, args.steps)}), flush=True)
         return 0
 
-    import linear_cross_entropy_fp32_amd as flce
-    from linear_cross_entropy_fp32_amd import _binding, synth
-
+    from linear_cross_entropy_fp32_amd import synth
     w = synth.WORKLOADS[args.workload]
-    dev = torch.device("cuda:0")
-    inp = synth.make_inputs(w)
-    h = inp.hidden.to(dev)
-    wt = inp.weight.to(dev)
-    b = None if inp.bias is None else inp.bias.to(dev)
-    t = inp.targets.to(dev)
-    go = inp.grad_out.to(dev).reshape(-1)
-    n, hd, v = w.n_tokens, w.hidden, w.vocab
-    prob = _binding.problem_for(h, wt, w.logit_scale, w.softcap, compact_valid=args.compact)
-    ws_bytes = flce.flce_workspace_bytes(prob)
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
-    f32 = dict(dtype=torch.float32, device=dev)
-    loss, lse, ent = (torch.empty(n, **f32) for _ in range(3))
-    hit = torch.empty(n, dtype=torch.uint8, device=dev)
-    red_f = torch.empty(3, **f32)
-    red_i = torch.empty(3, dtype=torch.int64, device=dev)
-    gh = torch.empty(n, hd, **f32)
-    gw = torch.empty(v, hd, **f32)
-    gb = torch.empty(v, **f32) if b is not None else None
-    mode = {"mean": 0, "sum": 1, "none": 2}[w.reduction]
-    L = flce.lib()
-    P = _binding._ptr
-    stream = torch.cuda.current_stream(dev)
-    sp = ctypes.c_void_p(stream.cuda_stream)
-
-    def fwd():
-        rc = L.flce_forward(ctypes.byref(prob), P(h), P(wt), P(b), P(t), P(loss), P(lse), P(ent),
-                            P(hit), None, P(red_f), P(red_i), P(ws), ws_bytes, sp)
-        if rc:
-            raise flce.FlceError(rc, flce.flce_last_error())
-
-    def bwd():
-        rc = L.flce_backward(ctypes.byref(prob), P(h), P(wt), P(b), P(t), P(lse), P(red_i), mode,
-                             P(go), P(gh), P(gw), P(gb), P(ws), ws_bytes, sp)
-        if rc:
-            raise flce.FlceError(rc, flce.flce_last_error())
-
-    for _ in range(args.warmup):
-        fwd()
-        bwd()
-    torch.cuda.synchronize()
-
-    # HIP events for the dominant kernel's launches, recorded by the library on
-    # the launch stream (flce_set_timing_events) over the whole timed region,
-    # and for the forward / backward split of every step; all timing-only
     hip = _hip_runtime()
-    n_chunks = _chunks_per_backward(prob)
-    n_pairs = args.steps * n_chunks + 1      # one spare pair: a full pool means overflow
-    n_step_ev = 3 * args.steps
-    evs = (ctypes.c_void_p * (2 * n_pairs + n_step_ev))()
-    for i in range(2 * n_pairs + n_step_ev):
-        _hip_ok(hip.hipEventCreateWithFlags(ctypes.byref(evs, i * ctypes.sizeof(ctypes.c_void_p)),
-                                            _EVENT_TIMING_ONLY))
-    step_ev = [evs[2 * n_pairs + i] for i in range(n_step_ev)]
-
-    def elapsed(a, b):
-        ms_i = ctypes.c_float(0.0)
-        _hip_ok(hip.hipEventElapsedTime(ctypes.byref(ms_i), ctypes.c_void_p(a), ctypes.c_void_p(b)))
-        return ms_i.value
-
-    def mark(e):
-        _hip_ok(hip.hipEventRecord(ctypes.c_void_p(e), sp))
-
-    start = torch.cuda.Event(enable_timing=True)
-    stop = torch.cuda.Event(enable_timing=True)
-    flce.flce_set_timing_events(_binding.FLCE_KERNEL_CONTRACT, evs, n_pairs)
-    torch.cuda.synchronize()
-    t_wall = time.perf_counter()
-    start.record(stream)
-    for i in range(args.steps):
-        mark(step_ev[3 * i])
-        fwd()
-        mark(step_ev[3 * i + 1])
-        bwd()
-        mark(step_ev[3 * i + 2])
-    stop.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t_wall
-    recorded = flce.flce_set_timing_events(_binding.FLCE_KERNEL_CONTRACT, None, 0)
-    if recorded >= n_pairs:
-        raise RuntimeError("more contraction launches than timing events: the per-step "
-                           "kernel time would be incomplete")
-    kern_ms = [elapsed(evs[2 * i], evs[2 * i + 1]) for i in range(recorded)]
-    step_ms = [elapsed(step_ev[3 * i], step_ev[3 * i + 2]) for i in range(args.steps)]
-    fwd_ms = sum(elapsed(step_ev[3 * i], step_ev[3 * i + 1]) for i in range(args.steps)) / args.steps
-    bwd_ms = sum(elapsed(step_ev[3 * i + 1], step_ev[3 * i + 2])
-                 for i in range(args.steps)) / args.steps
-    for i in range(2 * n_pairs + n_step_ev):
-        hip.hipEventDestroy(ctypes.c_void_p(evs[i]))
-    total_ms = start.elapsed_time(stop)
-    ms = total_ms / args.steps
-
-    # cold steps: every step starts with L2 and MALL (256 MB) holding none of
-    # its operands, after a 512 MiB write outside the step's event bracket
-    cold_ms = []
-    if args.cold_steps > 0:
-        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
-        cev = (ctypes.c_void_p * (2 * args.cold_steps))()
-        for i in range(2 * args.cold_steps):
-            _hip_ok(hip.hipEventCreateWithFlags(
-                ctypes.byref(cev, i * ctypes.sizeof(ctypes.c_void_p)), _EVENT_TIMING_ONLY))
-        for i in range(args.cold_steps):
-            flush.fill_(i & 255)
-            mark(cev[2 * i])
-            fwd()
-            bwd()
-            mark(cev[2 * i + 1])
-        torch.cuda.synchronize()
-        cold_ms = [elapsed(cev[2 * i], cev[2 * i + 1]) for i in range(args.cold_steps)]
-        for i in range(2 * args.cold_steps):
-            hip.hipEventDestroy(ctypes.c_void_p(cev[i]))
-        del flush
+    r = Runner(w, args.compact)
+    m = measure(r, args.steps, args.warmup, hip, kernel_events=True)
+    n, hd, v = w.n_tokens, w.hidden, w.vocab
+    ms = pct(m["cold"], 50)
     # with compaction the algorithmic work is that of the rows carrying a loss
-    n_work = int(red_i[0].item()) if args.compact else n
+    n_valid = int(r.red_i[0].item())
+    n_work = n_valid if args.compact else n
     flops = 8.0 * n_work * hd * v
     tflops = flops / (ms * 1e-3) / 1e12
     # dominant kernel: the backward contraction (grad_hidden and grad_weight of
     # one vocabulary chunk per launch); over a step its launches do 4*N*H*V
     # flops of algorithmic work
+    kern_ms = m["kern_ms"]
     launches = max(1, len(kern_ms))
     kern_avg = sum(kern_ms) / launches if kern_ms else float("nan")
     per_step_ms = kern_avg * launches / args.steps
     kern_tflops = 4.0 * n_work * hd * v / (per_step_ms * 1e-3) / 1e12
     traffic = _committed_traffic(w.name, "contract_kernel")
+    warm_ms = pct(m["warm"], 50)
     out = {
         "metric": METRIC, "value": n / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "steps": args.steps, "warmup": m["warmup_steps"], "ms_per_step": ms,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": w.name, "n_tokens": n, "hidden": hd, "vocab": v,
                    "hidden_dtype": w.hidden_dtype, "bias": w.bias, "logit_scale": w.logit_scale,
                    "softcap": w.softcap, "reduction": w.reduction,
-                   "compact_valid": bool(args.compact), "n_valid": int(red_i[0].item())},
+                   "compact_valid": bool(args.compact), "n_valid": n_valid},
+        "timing": "median of K steps, each after a 512 MiB L2+MALL eviction outside its "
+                  "events; warmup >= 25 ms after one discarded call",
         "tflops": tflops, "pct_bf16_peak": 100.0 * tflops / PEAK_BF16_TFLOPS,
-        "fwd_ms": fwd_ms, "bwd_ms": bwd_ms, "wall_s": wall,
-        "step_ms_p20_p50_p80": [float(np.percentile(step_ms, q)) for q in (20, 50, 80)],
-        "cold_step_ms_p20_p50_p80": ([float(np.percentile(cold_ms, q)) for q in (20, 50, 80)]
-                                     if cold_ms else None),
+        "fwd_ms": pct(m["fwd"], 50), "bwd_ms": pct(m["bwd"], 50), "wall_s": m["wall_s"],
+        "warmup_ms": m["warmup_ms"],
+        "step_ms_p20_p50_p80": [pct(m["cold"], q) for q in (20, 50, 80)],
+        "warm_ms_per_step": warm_ms,
+        "warm_step_ms_p20_p50_p80": [pct(m["warm"], q) for q in (20, 50, 80)],
+        "warm_tokens_per_s": n / (warm_ms * 1e-3),
         "roofline": {"bound": "mfma", "kernel": "contract_kernel", "achieved": kern_tflops,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": kern_tflops / PEAK_BF16_TFLOPS, "traffic": traffic,
                      "launch_ms": kern_avg, "launches_per_step": launches / args.steps},
     }
+    del r
+    torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(w, synth.make_inputs(w), args.cpu_seconds)
+    if args.per_config_steps > 0 and not args.compact:
+        out["per_config"] = per_config(args, hip)
     print(json.dumps(out), flush=True)
     return 0
 

@@ -202,7 +202,7 @@ def grad_raw_logits(z: np.ndarray, t: np.ndarray, gn: np.ndarray, valid: np.ndar
 def backward(hidden: np.ndarray, weight: np.ndarray, bias: Optional[np.ndarray],
              targets: np.ndarray, prob: Problem, mode: str, grad_out,
              need_weight: bool = True, rows: Optional[np.ndarray] = None,
-             vocab_rows: Optional[np.ndarray] = None) -> dict:
+             vocab_rows: Optional[np.ndarray] = None, sketch=None) -> dict:
     """grad_hidden, grad_weight and grad_bias of the reduced loss.
 
     grad_hidden[n] = sum_v d[n, v] W[v]; grad_weight[v] = sum_n d[n, v] h[n];
@@ -212,6 +212,17 @@ def backward(hidden: np.ndarray, weight: np.ndarray, bias: Optional[np.ndarray],
     ``rows`` restricts grad_hidden to those rows (it only needs their own
     logits).  ``vocab_rows`` restricts grad_weight / grad_bias to those vocab
     entries; they still need every row's softmax, so all rows are projected.
+
+    ``sketch = (sigma, rho)``, sign matrices of shapes [K, N] and [K, V], adds
+    fixed linear summaries of the whole gradients (test infrastructure, for
+    checking outputs too large to store):
+      sketch_grad_hidden[k] = sum_n sigma[k, n] grad_hidden[n]
+                            = (sum_n sigma[k, n] d[n, :]) @ W,
+      sketch_grad_weight[k] = sum_v rho[k, v] grad_weight[v]
+                            = sum_n (sum_v rho[k, v] d[n, v]) h[n],
+      sketch_grad_bias[k]   = sum_v rho[k, v] grad_bias[v];
+    the right-hand sides are the same sums with the order of summation
+    exchanged, so no full gradient has to be formed.
     """
     h = np.asarray(hidden, dtype=np.float64)
     w = np.asarray(weight, dtype=np.float64)
@@ -240,6 +251,13 @@ def backward(hidden: np.ndarray, weight: np.ndarray, bias: Optional[np.ndarray],
     nv = vocab if vsel is None else len(vsel)
     gw = np.zeros((nv, h.shape[1]))
     gb = np.zeros(nv)
+    if sketch is not None:
+        sigma = np.asarray(sketch[0], dtype=np.float64)
+        rho = np.asarray(sketch[1], dtype=np.float64)
+        assert sigma.shape[1] == n and rho.shape[1] == vocab and sigma.shape[0] == rho.shape[0]
+        sd = np.zeros((sigma.shape[0], vocab))          # sum_n sigma[k, n] d[n, :]
+        sk_gw = np.zeros((rho.shape[0], h.shape[1]))
+        sk_gb = np.zeros(rho.shape[0])
     for r0, r1 in _row_blocks(n, vocab):
         z = final_logits(h[r0:r1], w, b, prob)
         d = grad_raw_logits(z, t[r0:r1], gn[r0:r1], valid[r0:r1], prob)
@@ -248,6 +266,15 @@ def backward(hidden: np.ndarray, weight: np.ndarray, bias: Optional[np.ndarray],
         dv = d if vsel is None else d[:, vsel]
         gw += dv.T @ h[r0:r1]
         gb += dv.sum(axis=0)
+        if sketch is not None:
+            sd += sigma[:, r0:r1] @ d
+            dr = d @ rho.T                               # [rows, K]
+            sk_gw += dr.T @ h[r0:r1]
+            sk_gb += dr.sum(axis=0)
+    if sketch is not None:
+        out["sketch_grad_hidden"] = sd @ w
+        out["sketch_grad_weight"] = sk_gw
+        out["sketch_grad_bias"] = sk_gb
     if vsel is None:
         out["grad_weight"] = gw
         out["grad_bias"] = gb

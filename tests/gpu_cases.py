@@ -9,6 +9,7 @@ on every row whose oracle top-2 margin is at least 1e-2.
 """
 from __future__ import annotations
 
+import os
 import sys
 
 import numpy as np
@@ -124,3 +125,73 @@ def check_grad(a: np.ndarray, b: np.ndarray, name: str, label: str = "") -> None
     assert e <= TOL_GRAD, f"{label} {name}: relative Frobenius error {e}"
     zero_rows = np.all(b == 0, axis=tuple(range(1, b.ndim))) if b.ndim > 1 else (b == 0)
     assert np.all(a[zero_rows] == 0), f"{label} {name}: nonzero where the oracle is exactly 0"
+
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def golden_oracle(gold, w, inp) -> dict:
+    """Per-token and reduced oracle values of a stored full-size golden."""
+    o = {k: gold[k] for k in ("loss", "lse", "entropy", "argmax", "hit", "margin")}
+    t = inp.targets.numpy()
+    o["valid"] = (t >= 0) & (t < w.vocab)
+    for k in ("loss_sum", "loss_mean", "entropy_sum"):
+        o[k] = float(gold[k])
+    for k in ("n_valid", "n_correct", "n_bad"):
+        o[k] = int(gold[k])
+    return o
+
+
+def check_fullsize_grads(g: dict, gold, w, inp, name: str) -> None:
+    """Gradients of a full-size run against a stored golden: grad_hidden rows
+    of every token tile; grad_weight / grad_bias rows around every chunk and
+    split-K slot edge, the rows that are some valid row's target and the
+    softmax-only rows each checked on their own; and the sign sketches of the
+    whole outputs (tests/golden/make_fullsize_golden.py)."""
+    t = inp.targets.numpy()
+    valid = (t >= 0) & (t < w.vocab)
+    if not valid.any():
+        for k in ("grad_hidden", "grad_weight"):
+            assert torch.count_nonzero(g[k]).item() == 0, k
+        if g.get("grad_bias") is not None:
+            assert torch.count_nonzero(g["grad_bias"]).item() == 0
+        return
+    rows, vrows = gold["rows"], gold["vocab_rows"]
+    gh, gw = g["grad_hidden"], g["grad_weight"]
+    check_grad(gh.numpy()[rows].astype(np.float64), gold["grad_hidden_rows"].astype(np.float64),
+               "grad_hidden rows", name)
+    is_t = np.isin(vrows, t[valid])
+    parts = ((is_t, "target"), (~is_t, "softmax-only"))
+    gwr = gw.numpy()[vrows].astype(np.float64)
+    ref = gold["grad_weight_rows"].astype(np.float64)
+    for sel, part in parts:
+        if sel.any():
+            check_grad(gwr[sel], ref[sel], f"grad_weight {part} rows", name)
+    if inp.bias is not None:
+        gbr = g["grad_bias"].numpy()[vrows].astype(np.float64)
+        rb = gold["grad_bias_rows"].astype(np.float64)
+        for sel, part in parts:
+            if sel.any():
+                check_grad(gbr[sel], rb[sel], f"grad_bias {part} rows", name)
+    if GOLDEN not in sys.path:
+        sys.path.insert(0, GOLDEN)
+    from make_fullsize_golden import sketch_signs
+    sigma, rho = sketch_signs(w.n_tokens, w.vocab, t)
+    sk_gh = (torch.from_numpy(sigma) @ gh.double()).numpy()
+    sk_gw = sum(torch.from_numpy(rho[:, v0:v0 + 16384]) @ gw[v0:v0 + 16384].double()
+                for v0 in range(0, w.vocab, 16384)).numpy()
+    check_grad(sk_gh, gold["sketch_grad_hidden"], "grad_hidden sketch", name)
+    check_grad(sk_gw[:2], gold["sketch_grad_weight"][:2], "grad_weight sketch", name)
+    check_grad(sk_gw[2:], gold["sketch_grad_weight"][2:], "grad_weight softmax-only sketch", name)
+    if inp.bias is not None:
+        sk_gb = (torch.from_numpy(rho) @ g["grad_bias"].double()).numpy()
+        check_grad(sk_gb[:2], gold["sketch_grad_bias"][:2], "grad_bias sketch", name)
+        check_grad(sk_gb[2:], gold["sketch_grad_bias"][2:], "grad_bias softmax-only sketch",
+                   name)
+
+
+def check_fullsize(g: dict, gold, w, inp, name: str) -> None:
+    o = golden_oracle(gold, w, inp)
+    check_tokens(g, o, label=name)
+    check_reduced(g, o, label=name)
+    check_fullsize_grads(g, gold, w, inp, name)

@@ -13,7 +13,8 @@ import torch
 import linear_cross_entropy_fp32_amd as flce
 from linear_cross_entropy_fp32_amd import _binding, synth
 from oracle import backward, forward
-from tests.gpu_cases import (check_compact_tokens, check_grad, check_reduced, prob_of, rel_fro,
+from tests.gpu_cases import (check_compact_tokens, check_fullsize_grads, check_grad,
+                             check_reduced, prob_of, rel_fro,
                              run_gpu, say, to_f64)
 
 pytestmark = pytest.mark.gpu
@@ -176,11 +177,4 @@ def test_fullsize_compact_against_stored_oracle(name):
         o[k] = int(gold[k])
     check_compact_tokens(g, o, _valid(inp, w.vocab), label=name)
     check_reduced(g, o, label=name)
-    rows, vrows = gold["rows"], gold["vocab_rows"]
-    check_grad(g["grad_hidden"].numpy()[rows], gold["grad_hidden_rows"], "grad_hidden rows", name)
-    check_grad(g["grad_weight"].numpy()[vrows], gold["grad_weight_rows"], "grad_weight rows", name)
-    if inp.bias is not None:
-        check_grad(g["grad_bias"].numpy()[vrows], gold["grad_bias_rows"], "grad_bias rows", name)
-    if o["n_valid"] == 0:
-        for k in ("grad_hidden", "grad_weight"):
-            assert torch.count_nonzero(g[k]).item() == 0, k
+    check_fullsize_grads(g, gold, w, inp, name)

@@ -21,6 +21,7 @@ PIN_TESTS = [
     (pins.test_num_items_divisor, {}),
     (pins.test_bad_targets_are_counted_and_ignored, {}),
     (pins.test_margin_against_topk, {}),
+    (pins.test_gradient_sketches_against_torch, {}),
 ]
 
 

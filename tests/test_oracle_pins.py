@@ -422,3 +422,32 @@ def test_many_row_blocks_against_torch():
     assert np.array_equal(f["argmax"], torch.argmax(z, dim=1).numpy())
     assert np.allclose(f["margin"], _topk_margin(z), atol=1e-12)
     assert math.isclose(f["loss_mean"], float(loss[valid].mean()), rel_tol=1e-12)
+
+
+def test_gradient_sketches_against_torch():
+    """The oracle's gradient sketches (fixed sign projections of the whole
+    gradients, used to check full-size outputs) equal the same projections of
+    torch's float64 autograd gradients, with and without bias and softcap, on
+    a shape cut into several row blocks.  Without a bias, torch's gradient
+    with respect to an all-zero bias stands in for grad_bias."""
+    import oracle.flce_oracle as orc
+    for bias, cap, red in ((True, 4.0, "none"), (False, 0.0, "mean"), (False, 2.0, "sum")):
+        n, h, v = 40, 6, 50
+        hid, w, b, t = _rand_problem(n, h, v, 77, bias=bias)
+        prob = Problem(logit_scale=0.8, softcap=cap)
+        rng = np.random.default_rng(3)
+        grad_out = rng.uniform(0, 2, n) if red == "none" else 1.3
+        sigma = rng.choice([-1.0, 1.0], size=(3, n))
+        rho = rng.choice([-1.0, 1.0], size=(3, v))
+        ref = _torch_reference(hid, w, b if bias else np.zeros(v), t, prob, red, grad_out)
+        real = orc._row_blocks
+        orc._row_blocks = lambda nn, vv, max_elems=1 << 24: real(nn, vv, max_elems=7 * vv)
+        try:
+            g = orc.backward(hid, w, b, t, prob, red, grad_out, rows=np.arange(0, n, 5),
+                             vocab_rows=np.array([0, v - 1]), sketch=(sigma, rho))
+        finally:
+            orc._row_blocks = real
+        assert np.allclose(g["sketch_grad_hidden"], sigma @ ref["gh"], atol=1e-12)
+        assert np.allclose(g["sketch_grad_weight"], rho @ ref["gw"], atol=1e-12)
+        assert np.allclose(g["sketch_grad_bias"], rho @ ref["gb"], atol=1e-12)
+        assert np.abs(g["sketch_grad_weight"]).max() > 1e-3

@@ -8,7 +8,8 @@ import torch
 import linear_cross_entropy_fp32_amd as flce
 from linear_cross_entropy_fp32_amd import synth
 from oracle import Problem, backward, final_logits, forward
-from tests.gpu_cases import (check_grad, check_reduced, check_tokens, prob_of, rel_fro, run_gpu,
+from tests.gpu_cases import (check_fullsize, check_grad, check_reduced, check_tokens, prob_of,
+                             rel_fro, run_gpu,
                              say, to_f64)
 
 pytestmark = pytest.mark.gpu
@@ -286,9 +287,11 @@ FULL = ["tiny", "huge_vocab", "bias_none", "zipf_sum", "fp32_hidden", "fp32_hidd
 def test_fullsize_against_stored_oracle(name):
     """The full workloads, in the launch configuration the bench times,
     against oracle values written by tests/golden/make_fullsize_golden.py:
-    every row's loss / entropy / lse / argmax / hit, the reductions, sampled
-    grad_hidden rows and sampled grad_weight / grad_bias rows.  The identity
-    sum_v <gw_v, W_v> = sum_n <gh_n, h_n> is checked over the whole outputs."""
+    every row's loss / entropy / lse / argmax / hit, the reductions,
+    grad_hidden rows of every token tile, grad_weight / grad_bias rows on
+    both sides of every chunk and split-K slot edge (the target-heavy rows and
+    the softmax-only rows each within the tolerance on their own), and sign
+    sketches of the whole gradients."""
     path = os.path.join(GOLDEN, f"fullsize_{name}.npz")
     if not os.path.exists(path):
         pytest.skip(f"{path} not generated")
@@ -297,27 +300,58 @@ def test_fullsize_against_stored_oracle(name):
     say(f"[parity] full size {name}: drawing inputs")
     inp = synth.make_inputs(w)
     assert synth.input_checksum(inp) == str(gold["checksum"]), "input generator drifted"
+    plan = flce.flce_plan_info(flce.make_problem(
+        w.n_tokens, w.hidden, w.vocab, hidden_dtype=1 if w.hidden_dtype == "f32" else 0,
+        weight_dtype=1 if w.weight_dtype == "f32" else 0))
+    assert plan["chunk_rows"] == int(gold["chunk_rows"]), "golden sampled another chunk plan"
+    assert plan["gh_rows_per_split"] == int(gold["gh_rows_per_split"])
     say(f"[parity] full size {name}: running")
     g = run_gpu(w, inp)
-    o = {k: gold[k] for k in ("loss", "lse", "entropy", "argmax", "hit", "margin")}
-    t = inp.targets.numpy()
-    o["valid"] = (t >= 0) & (t < w.vocab)
-    for k in ("loss_sum", "loss_mean", "entropy_sum"):
-        o[k] = float(gold[k])
-    for k in ("n_valid", "n_correct", "n_bad"):
-        o[k] = int(gold[k])
-    check_tokens(g, o, label=name)
-    check_reduced(g, o, label=name)
-    rows, vrows = gold["rows"], gold["vocab_rows"]
-    check_grad(g["grad_hidden"].numpy()[rows], gold["grad_hidden_rows"], "grad_hidden rows", name)
-    check_grad(g["grad_weight"].numpy()[vrows], gold["grad_weight_rows"], "grad_weight rows", name)
-    if inp.bias is not None:
-        check_grad(g["grad_bias"].numpy()[vrows], gold["grad_bias_rows"], "grad_bias rows", name)
-    if o["n_valid"] == 0:
-        for k in ("grad_hidden", "grad_weight"):
-            assert torch.count_nonzero(g[k]).item() == 0, k
-        return
-    lhs = float((g["grad_weight"].double() * inp.weight.double()).sum())
-    rhs = float((g["grad_hidden"].double() * inp.hidden.double()).sum())
-    scale = float(g["grad_weight"].double().norm() * inp.weight.double().norm())
-    assert abs(lhs - rhs) <= 1e-2 * scale, (lhs, rhs, scale)
+    check_fullsize(g, gold, w, inp, name)
+
+
+@pytest.mark.parametrize("name", ["zipf_sum", "huge_vocab", "bias_none"])
+def test_fullsize_argmax_targets_give_exact_accuracy(name):
+    """The pages' accuracy experiment at full size: every target set to the
+    oracle's argmax of the final logits (stored in the golden), forward only;
+    each row whose top-2 margin is at least 1e-2 must be a hit, and the
+    argmax must agree there.  At logit scale 1/16 (zipf_sum) the final logits
+    have a spread of ~0.04, so most rows sit under the margin and this is
+    where the near-tie handling is exercised; the sure rows still number in
+    the thousands."""
+    path = os.path.join(GOLDEN, f"fullsize_{name}.npz")
+    if not os.path.exists(path):
+        pytest.skip(f"{path} not generated")
+    gold = np.load(path, allow_pickle=False)
+    w = synth.WORKLOADS[name]
+    inp = synth.make_inputs(w)
+    assert synth.input_checksum(inp) == str(gold["checksum"]), "input generator drifted"
+    inp.targets = torch.from_numpy(gold["argmax"].astype(np.int64))
+    sure = gold["margin"] >= 1e-2
+    say(f"[parity] full size {name}, argmax targets: {int(sure.sum())} sure rows")
+    g = run_gpu(w, inp, backward=False)
+    hit = g["hit"].numpy()
+    assert np.all(hit[sure] == 1), int((hit[sure] == 0).sum())
+    assert np.array_equal(g["argmax"].numpy()[sure], gold["argmax"][sure])
+    assert int(g["reduced_i64"][1]) == int(hit.astype(np.int64).sum())
+    assert int(g["reduced_i64"][0]) == w.n_tokens
+    assert sure.sum() >= 1000
+
+
+def test_argmax_targets_zipf_shape_class():
+    """The same experiment on a fresh draw of the zipf_sum shape class (H =
+    1024, V = 151936, logit scale 1/16, no softcap) with the oracle computed
+    here: 1024 tokens."""
+    w = synth.Workload("argmax_zipf_class", 1024, 1024, 151936, logit_scale=0.0625,
+                       targets="zipf", ignore_every=0, reduction="sum", seed=4321)
+    inp = synth.make_inputs(w)
+    z = final_logits(to_f64(inp.hidden), to_f64(inp.weight), None, prob_of(w))
+    am = np.argmax(z, axis=1)
+    top2 = np.partition(z, w.vocab - 2, axis=1)[:, w.vocab - 2:]
+    sure = (top2[:, 1] - top2[:, 0]) >= 1e-2
+    inp.targets = torch.from_numpy(am.astype(np.int64))
+    say(f"[parity] argmax targets, zipf shape class: {int(sure.sum())} sure rows")
+    g = run_gpu(w, inp, backward=False)
+    assert np.all(g["hit"].numpy()[sure] == 1)
+    assert np.array_equal(g["argmax"].numpy()[sure], am[sure])
+    assert sure.sum() >= 100

@@ -118,3 +118,48 @@ def test_plan_info_errors():
     assert lib.flce_plan_info(ctypes.byref(flce.make_problem(4, 64, 10)), None, 3) == -1
     out = (ctypes.c_int64 * 2)()
     assert lib.flce_plan_info(ctypes.byref(flce.make_problem(4, 64, 10)), out, 2) == 2
+
+
+def _golden_names():
+    import glob
+    import os
+    root = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+    return sorted(os.path.basename(p)[len("fullsize_"):-len(".npz")]
+                  for p in glob.glob(os.path.join(root, "fullsize_*.npz")))
+
+
+@pytest.mark.parametrize("name", _golden_names())
+def test_golden_sampling_matches_the_plan(name):
+    """The stored full-size goldens sampled the chunks and split-K slots the
+    library actually plans: the recorded chunk plan equals flce_plan_info's,
+    every backward chunk holds at least two sampled grad_weight rows with both
+    of its edge rows among them, every split-K slot edge has a sampled row on
+    each side, and every 256-token tile has a sampled grad_hidden row."""
+    import os
+
+    import numpy as np
+
+    from linear_cross_entropy_fp32_amd import synth
+    w = synth.WORKLOADS[name]
+    gold = np.load(os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden",
+                                f"fullsize_{name}.npz"), allow_pickle=False)
+    if "chunk_rows" not in gold.files:
+        pytest.skip("golden written before the chunk plan was recorded")
+    p = flce.make_problem(w.n_tokens, w.hidden, w.vocab,
+                          hidden_dtype=1 if w.hidden_dtype == "f32" else 0,
+                          weight_dtype=1 if w.weight_dtype == "f32" else 0)
+    pl = flce.flce_plan_info(p)
+    vc, kps = pl["chunk_rows"], pl["gh_rows_per_split"]
+    assert vc == int(gold["chunk_rows"]) and kps == int(gold["gh_rows_per_split"])
+    vrows = set(int(x) for x in gold["vocab_rows"])
+    for c0 in range(0, w.vocab, vc):
+        c1 = min(w.vocab, c0 + vc)
+        assert {c0, c1 - 1} <= vrows, (c0, c1)
+        assert len([x for x in vrows if c0 <= x < c1]) >= 2
+        for e in range(c0 + kps, c1, kps):
+            assert {e - 1, e} <= vrows, e
+    rows = set(int(x) for x in gold["rows"])
+    for t0 in range(0, w.n_tokens, 256):
+        assert any(t0 <= r < t0 + 256 for r in rows), t0
+    for k in ("sketch_grad_hidden", "sketch_grad_weight", "sketch_grad_bias"):
+        assert k in gold.files
