@@ -127,11 +127,30 @@ int flce_workspace_bytes(const flce_problem* p, size_t* bytes);
  *                    is always written), hit [N] uint8, argmax [N] int32 or NULL,
  *   reduced_f32 [3]: loss_sum, loss_mean, entropy_sum (over valid rows)
  *   reduced_i64 [3]: n_valid, n_correct, n_bad_target
- * workspace: >= flce_workspace_bytes(), 256-byte aligned. */
+ * workspace: 256-byte aligned, at least the forward's part of the plan
+ * (flce_plan_info field 9); flce_workspace_bytes() always suffices. */
 int flce_forward(const flce_problem* p, const void* hidden, const void* weight,
                  const float* bias, const int64_t* targets, float* loss, float* lse,
                  float* entropy, uint8_t* hit, int32_t* argmax, float* reduced_f32,
                  int64_t* reduced_i64, void* workspace, size_t workspace_bytes, void* stream);
+
+/* flce_forward without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, outputs and errors as
+ * flce_forward; the forward's partial states live in a scratch array that the
+ * library holds in device memory, 16 MiB per GPU, from the first call on that
+ * GPU until the process ends (the device is the one `stream` belongs to).
+ * Nothing is allocated: a problem whose forward needs more than 16 MiB of
+ * scratch (flce_plan_info field 9: e.g. fp32 hidden states, whose bf16 split
+ * alone is 4*N*H bytes) returns FLCE_ERR_WORKSPACE before anything is
+ * launched.  Every call on one GPU shares that GPU's array: calls that
+ * overlap on one GPU (other streams, other threads) race, so serialise them.
+ * The first call on a device also looks the array's address up (no
+ * allocation, no kernel). */
+int flce_forward_noalloc(const flce_problem* p, const void* hidden, const void* weight,
+                         const float* bias, const int64_t* targets, float* loss, float* lse,
+                         float* entropy, uint8_t* hit, int32_t* argmax, float* reduced_f32,
+                         int64_t* reduced_i64, void* stream);
 
 /* Backward of the reduced loss: grad_hidden, grad_weight, grad_bias.
  * Defined by the first TRL page's review, "Correctness" item 2 (the backward

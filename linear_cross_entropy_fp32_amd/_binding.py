@@ -22,7 +22,8 @@ ERROR_NAMES = {-1: "FLCE_ERR_NULL", -2: "FLCE_ERR_SHAPE", -3: "FLCE_ERR_DTYPE",
                -4: "FLCE_ERR_ALIGN", -5: "FLCE_ERR_WORKSPACE", -6: "FLCE_ERR_HIP",
                -7: "FLCE_ERR_ARG"}
 EXPORTED = ("flce_validate", "flce_workspace_bytes", "flce_forward", "flce_backward",
-            "flce_last_error", "flce_abi_version", "flce_set_timing_events", "flce_plan_info")
+            "flce_last_error", "flce_abi_version", "flce_set_timing_events", "flce_plan_info",
+            "flce_forward_noalloc")
 PLAN_FIELDS = ("chunk_rows", "n_chunks", "fwd_splits", "fwd_tiles_per_split",
                "dz_tiles_per_wg", "gh_splits", "gh_rows_per_split", "window_token_tiles",
                "token_tile_fastest", "fwd_workspace_bytes", "bwd_workspace_bytes",
@@ -65,6 +66,9 @@ def lib() -> ctypes.CDLL:
         L.flce_forward.argtypes = [pp, vp, vp, f32p, i64p, f32p, f32p, f32p, vp, vp, f32p, i64p,
                                    vp, ctypes.c_size_t, vp]
         L.flce_forward.restype = ctypes.c_int
+        L.flce_forward_noalloc.argtypes = [pp, vp, vp, f32p, i64p, f32p, f32p, f32p, vp, vp,
+                                           f32p, i64p, vp]
+        L.flce_forward_noalloc.restype = ctypes.c_int
         L.flce_backward.argtypes = [pp, vp, vp, f32p, i64p, f32p, i64p, ctypes.c_int, f32p,
                                     f32p, f32p, f32p, vp, ctypes.c_size_t, vp]
         L.flce_backward.restype = ctypes.c_int
@@ -202,6 +206,35 @@ def flce_forward(hidden: torch.Tensor, weight: torch.Tensor, targets: torch.Tens
         _ptr(out["loss"]), _ptr(out["lse"]), _ptr(out["entropy"]), _ptr(out["hit"]),
         _ptr(out["argmax"]), _ptr(out["reduced_f32"]), _ptr(out["reduced_i64"]),
         _ptr(workspace), workspace.numel(), _stream(dev)))
+    return out
+
+
+def flce_forward_noalloc(hidden: torch.Tensor, weight: torch.Tensor, targets: torch.Tensor,
+                         bias: Optional[torch.Tensor] = None, logit_scale: float = 1.0,
+                         softcap: Optional[float] = None, ignore_index: int = -100,
+                         mean_divisor: float = 0.0, out: Optional[dict] = None) -> dict:
+    """Run ``flce_forward_noalloc`` (no workspace: the library's per-GPU
+    scratch) on the current stream, into ``out`` (the same keys as
+    ``flce_forward`` returns) or into new tensors."""
+    if targets is None:
+        raise ValueError("targets are required")
+    dev = weight.device
+    for t, nm in ((hidden, "hidden"), (weight, "weight"), (targets, "targets")):
+        _require(t, nm, dev)
+    prob = problem_for(hidden, weight, logit_scale, softcap, ignore_index, mean_divisor)
+    n = hidden.shape[0]
+    if out is None:
+        f32 = dict(dtype=torch.float32, device=dev)
+        out = dict(loss=torch.empty(n, **f32), lse=torch.empty(n, **f32),
+                   entropy=torch.empty(n, **f32),
+                   hit=torch.empty(n, dtype=torch.uint8, device=dev),
+                   argmax=torch.empty(n, dtype=torch.int32, device=dev),
+                   reduced_f32=torch.empty(3, **f32),
+                   reduced_i64=torch.empty(3, dtype=torch.int64, device=dev))
+    _check(lib().flce_forward_noalloc(
+        ctypes.byref(prob), _ptr(hidden), _ptr(weight), _ptr(bias), _ptr(targets),
+        _ptr(out["loss"]), _ptr(out["lse"]), _ptr(out["entropy"]), _ptr(out["hit"]),
+        _ptr(out["argmax"]), _ptr(out["reduced_f32"]), _ptr(out["reduced_i64"]), _stream(dev)))
     return out
 
 

@@ -7,6 +7,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "flce.h"
 #include "flce_internal.h"
@@ -335,6 +336,41 @@ int prepare_rows(const flce_problem* p, const Plan& pl, const void* hidden, cons
   return FLCE_OK;
 }
 
+// Scratch of the allocation-free forward (flce_forward_noalloc): one copy of
+// this array per GPU, held until the process ends.  Host code never uses the
+// array's name as an address: the device address of each GPU's copy is looked
+// up once per device (hipGetSymbolAddress, with that device current) and kept.
+constexpr size_t kScratchBytes = size_t(16) << 20;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the device that `s` belongs to.
+int scratch_for_stream(hipStream_t s, void** out) {
+  hipDevice_t dev = 0;
+  int rc;
+  if ((rc = hip_check(hipStreamGetDevice(s, &dev), "hipStreamGetDevice"))) return rc;
+  if (dev < 0 || dev >= kMaxDevices) return fail(FLCE_ERR_ARG, "device %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    int cur = 0;
+    if ((rc = hip_check(hipGetDevice(&cur), "hipGetDevice"))) return rc;
+    if (cur != dev && (rc = hip_check(hipSetDevice(dev), "hipSetDevice"))) return rc;
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    const hipError_t e2 = cur != dev ? hipSetDevice(cur) : hipSuccess;
+    if ((rc = hip_check(e, "hipGetSymbolAddress(scratch)"))) return rc;
+    if ((rc = hip_check(e2, "hipSetDevice (restore)"))) return rc;
+    if (!ptr || reinterpret_cast<uintptr_t>(ptr) % kAlign != 0)
+      return fail(FLCE_ERR_HIP, "scratch address %p is not 256-byte aligned", ptr);
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return FLCE_OK;
+}
+
 }  // namespace
 }  // namespace flce
 
@@ -410,9 +446,9 @@ int flce_forward(const flce_problem* p, const void* hidden, const void* weight,
     return fail(FLCE_ERR_ALIGN, "bias/targets/outputs misaligned for their dtype");
   if (!aligned(workspace, kAlign)) return fail(FLCE_ERR_ALIGN, "workspace must be 256-byte aligned");
   const Plan pl = make_plan(p);
-  if (workspace_bytes < pl.bytes)
+  if (workspace_bytes < pl.fwd_bytes)
     return fail(FLCE_ERR_WORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes,
-                pl.bytes);
+                pl.fwd_bytes);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
 
@@ -466,6 +502,26 @@ int flce_forward(const flce_problem* p, const void* hidden, const void* weight,
   return hip_check(launch_fwd_finalize(f, pl.fin_blocks, p->mean_divisor > 0 ? p->mean_divisor : 0.f,
                                        reduced_f32, reduced_i64, rows.n_bad, s),
                    "fwd_finalize");
+}
+
+int flce_forward_noalloc(const flce_problem* p, const void* hidden, const void* weight,
+                         const float* bias, const int64_t* targets, float* loss, float* lse,
+                         float* entropy, uint8_t* hit, int32_t* argmax, float* reduced_f32,
+                         int64_t* reduced_i64, void* stream) {
+  g_err[0] = 0;
+  const int rc = validate(p);
+  if (rc) return rc;
+  const size_t need = make_plan(p).fwd_bytes;
+  if (need > kScratchBytes)
+    return fail(FLCE_ERR_WORKSPACE,
+                "flce_forward_noalloc: this problem needs %zu bytes of scratch, more than the "
+                "%zu bytes it holds (use flce_forward with a workspace)",
+                need, kScratchBytes);
+  void* ws = nullptr;
+  const int rc2 = scratch_for_stream(reinterpret_cast<hipStream_t>(stream), &ws);
+  if (rc2) return rc2;
+  return flce_forward(p, hidden, weight, bias, targets, loss, lse, entropy, hit, argmax,
+                      reduced_f32, reduced_i64, ws, kScratchBytes, stream);
 }
 
 int flce_backward(const flce_problem* p, const void* hidden, const void* weight,

@@ -172,3 +172,18 @@ def test_timing_hook_arguments():
     assert lib.flce_set_timing_events(flce.FLCE_KERNEL_CONTRACT, events, 1) == 0
     assert lib.flce_set_timing_events(flce.FLCE_KERNEL_CONTRACT, None, 0) == 0
 
+
+
+def test_noalloc_forward_rejects_oversized_problem():
+    """flce_forward_noalloc holds 16 MiB of scratch per GPU: a forward that
+    needs more (fp32 hidden states at 16384 x 4096, whose bf16 split alone is
+    268 MB) is refused with FLCE_ERR_WORKSPACE before any HIP call."""
+    lib = flce.lib()
+    p = flce.make_problem(16384, 4096, 151936, hidden_dtype=flce.FLCE_F32)
+    assert flce.flce_plan_info(p)["fwd_workspace_bytes"] > 16 << 20
+    A = _fake(0x100000)
+    rc = lib.flce_forward_noalloc(ctypes.byref(p), A, A, None, A, A, A, A, A, None, A, A, None)
+    assert rc == -5
+    assert "16777216" in flce.flce_last_error()
+    assert flce.flce_plan_info(flce.make_problem(2048, 640, 262144))["fwd_workspace_bytes"] \
+        <= 16 << 20
