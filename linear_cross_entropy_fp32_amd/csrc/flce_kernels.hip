@@ -111,23 +111,27 @@ __device__ __forceinline__ float final_u(float x, float kx, float bk, float c1, 
   }
 }
 
-// Bias terms (b * kx) of the kQ rows a lane holds in a wave's slab of rows;
-// rows past the vocabulary read zero through the buffer bound.
+// Bias values of the rows q = 4a .. 4a+3 of a lane's token column (rows
+// q_row(q) + 4 half of the wave's slab), read from the wave's row-DMA block of
+// the tile (see RowDma): one 16-byte LDS read.  Rows past the vocabulary hold
+// zero.
 template <bool BIAS>
-__device__ __forceinline__ void load_bias(const float* bias, int v, int vw, float kx,
-                                          float (&bk)[kQ]) {
+__device__ __forceinline__ void bias4(const float* blk, int a, int half, float (&b)[4]) {
   if constexpr (BIAS) {
-    const int half = (threadIdx.x & 63) >> 5;
-    const __amdgpu_buffer_rsrc_t rs = tile_rsrc(bias, (int64_t)v * 4);
-#pragma unroll
-    for (int q = 0; q < kQ; ++q) {
-      const uint32_t off = (uint32_t)(vw + q_row(q) + half * 4) * 4;
-      bk[q] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0)) * kx;
-    }
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    const f32x4 v = *reinterpret_cast<const f32x4*>(blk + q_row(4 * a) + half * 4);
+    b[0] = v[0];
+    b[1] = v[1];
+    b[2] = v[2];
+    b[3] = v[3];
   } else {
-#pragma unroll
-    for (int q = 0; q < kQ; ++q) bk[q] = 0.f;
+    b[0] = b[1] = b[2] = b[3] = 0.f;
   }
+}
+
+// The wave's 64-value block of tile t in the row-DMA buffers at `rows`.
+__device__ __forceinline__ const float* bias_block(const float* rows, int t) {
+  return rows + (t % kRowDmaBufs) * 256 + (threadIdx.x >> 6) * 64;
 }
 
 // --------------------------------------------------- fp32 hidden: hi / lo split
@@ -378,26 +382,36 @@ struct FwdEpilogue {
   const FwdArgs& a;
   PartState (&st)[kColumns];
   const int (&tgt)[kColumns];
+  const float* rows;               // row-DMA buffers of the bias (BIAS)
   int vt_begin, wm, half;
 
   __device__ __forceinline__ void operator()(int t, LogitTile& T, char*) {
     const int v0 = (vt_begin + t) * kLogitTileV;
     const int vw = v0 + wm * kWaveRows;
     const bool tail = v0 + kLogitTileV > a.v;
-    float bk[kQ];
-    load_bias<BIAS>(a.bias, a.v, vw, a.kx, bk);
+    const float* blk = BIAS ? bias_block(rows, t) : nullptr;
 #pragma unroll
     for (int j = 0; j < kColumns; ++j) {
+      // the bias values are read again for every column, four at a time, so
+      // that they are never all live next to the accumulators
+      if constexpr (BIAS) asm volatile("" ::: "memory");
       float val[kQ];
 #pragma unroll
-      for (int q = 0; q < kQ; ++q) {
-        const float x = T.acc[q >> 4][j][q & 15];
-        if constexpr (FIXED) {
-          const float e = fast_exp2(fmaf(x, a.kx, bk[q]));
-          val[q] = -a.c2 * fast_rcp(e + 1.0f);
-        } else {
-          float r;
-          val[q] = final_u<CAP>(x, a.kx, bk[q], a.c1, a.c2, r);
+      for (int g = 0; g < kQ / 4; ++g) {
+        float b[4];
+        bias4<BIAS>(blk, g, half, b);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int q = 4 * g + e;
+          // (x + b) * s in base-2 units: the product, then the bias, then the scale
+          const float x = BIAS ? T.acc[q >> 4][j][q & 15] + b[e] : T.acc[q >> 4][j][q & 15];
+          if constexpr (FIXED) {
+            const float ex = fast_exp2(x * a.kx);
+            val[q] = -a.c2 * fast_rcp(ex + 1.0f);
+          } else {
+            float r;
+            val[q] = final_u<CAP>(x, a.kx, 0.f, a.c1, a.c2, r);
+          }
         }
       }
       if (tail) {
@@ -445,10 +459,15 @@ fwd_stats_kernel(const FwdArgs a) {
   const Operand opA1{a.w1 ? a.w1 : a.w, a.hdim, vt_begin * kLogitTileV, a.v, a.hdim};
   const Operand opB0{a.h0, a.hdim, n0, n_rows, a.hdim};
   const Operand opB1{a.h1 ? a.h1 : a.h0, a.hdim, n0, n_rows, a.hdim};
-  FwdEpilogue<CAP, FIXED, BIAS> epi{a, st, tgt, vt_begin, wm, half};
+  __shared__ __attribute__((aligned(16))) float rows[BIAS ? kRowDmaBytes / 4 : 4];
+  RowDma rd{};
+  if constexpr (BIAS)
+    rd = RowDma{dma_rsrc(a.bias, (int64_t)a.v * 4), lds_addr(reinterpret_cast<char*>(rows)),
+                vt_begin * kLogitTileV};
+  FwdEpilogue<CAP, FIXED, BIAS> epi{a, st, tgt, rows, vt_begin, wm, half};
   LogitTile T;
-  T.run_stream<WSPLIT>(lds, opA0, opA1, opB0, opB1,
-                       logit_segments(a.h1 != nullptr, WSPLIT), a.hdim, ntiles, epi);
+  T.run_stream<WSPLIT, BIAS>(lds, opA0, opA1, opB0, opB1,
+                             logit_segments(a.h1 != nullptr, WSPLIT), a.hdim, ntiles, epi, rd);
 
 #pragma unroll
   for (int j = 0; j < kColumns; ++j) {
@@ -644,6 +663,7 @@ struct DzEpilogue {
   const float (&gs)[kColumns];     // g_n * s (times 4 with softcap: the slope is 4 r (1-r))
   const float (&nl)[kColumns];     // -lse_n in base-2 units
   const int (&tgt)[kColumns];
+  const float* rows;               // row-DMA buffers of the bias (BIAS)
   int vt_begin, wm, half, nbase;   // nbase: first token of the wave's columns
 
   __device__ __forceinline__ void operator()(int t, LogitTile& T, char* free_lds) {
@@ -651,8 +671,7 @@ struct DzEpilogue {
     const int v0 = a.c0 + (vt_begin + t) * kLogitTileV;
     const int vw = __builtin_amdgcn_readfirstlane(v0 + wm * kWaveRows);
     const bool tail = v0 + kLogitTileV > a.v;
-    float bk[kQ];
-    load_bias<BIAS>(a.bias, a.v, vw, a.kx, bk);
+    const float* blk = BIAS ? bias_block(rows, t) : nullptr;
     // [32 tokens][64 vocabulary rows] bf16 of this wave; the 8-byte piece p of
     // token row tl is stored at piece p ^ (tl / 2), which keeps both the
     // 8-byte writes and the 16-byte reads below free of bank conflicts
@@ -668,28 +687,42 @@ struct DzEpilogue {
                           (vw - a.c0) * 2;
 #pragma unroll
     for (int j = 0; j < kColumns; ++j) {
+      // the bias values are read again for every column, four at a time, so
+      // that they are never all live next to the accumulators
+      if constexpr (BIAS) asm volatile("" ::: "memory");
       float d[kQ];
 #pragma unroll
-      for (int q = 0; q < kQ; ++q) {
-        const float x = T.acc[q >> 4][j][q & 15];
-        if constexpr (CAP) {
-          const float e = fast_exp2(fmaf(x, a.kx, bk[q]));
-          const float r = fast_rcp(e + 1.0f);
-          const float p = fast_exp2(fmaf(-a.c2, r, a.c1 + nl[j]));
-          d[q] = p * (fmaf(-r, r, r) * gs[j]);       // g s p (1 - tanh^2), gs carries the 4
-        } else {
-          d[q] = fast_exp2(fmaf(x, a.kx, bk[q] + nl[j])) * gs[j];
+      for (int g = 0; g < kQ / 4; ++g) {
+        float b[4];
+        // with a bias, one group's reads at a time (the scheduler would
+        // otherwise hoist all eight and spill)
+        if constexpr (BIAS) __builtin_amdgcn_sched_barrier(0);
+        bias4<BIAS>(blk, g, half, b);
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) {
+          const int q = 4 * g + e4;
+          const float x = BIAS ? T.acc[q >> 4][j][q & 15] + b[e4] : T.acc[q >> 4][j][q & 15];
+          if constexpr (CAP) {
+            const float e = fast_exp2(x * a.kx);
+            const float r = fast_rcp(e + 1.0f);
+            const float p = fast_exp2(fmaf(-a.c2, r, a.c1 + nl[j]));
+            d[q] = p * (fmaf(-r, r, r) * gs[j]);     // g s p (1 - tanh^2), gs carries the 4
+          } else {
+            d[q] = fast_exp2(fmaf(x, a.kx, nl[j])) * gs[j];
+          }
         }
       }
       // one-hot term, only in lanes whose target row is one of their rows
       {
         const int rel = tgt[j] - vw - half * 4;
         if (rel >= 0 && rel < kWaveRows && (rel & 4) == 0) {
+          const float bt = BIAS ? blk[rel + half * 4] : 0.f;
 #pragma unroll
           for (int q = 0; q < kQ; ++q)
             if (q_row(q) == rel) {
               if constexpr (CAP) {
-                const float e = fast_exp2(fmaf(T.acc[q >> 4][j][q & 15], a.kx, bk[q]));
+                const float x = BIAS ? T.acc[q >> 4][j][q & 15] + bt : T.acc[q >> 4][j][q & 15];
+                const float e = fast_exp2(x * a.kx);
                 const float r = fast_rcp(e + 1.0f);
                 d[q] -= fmaf(-r, r, r) * gs[j];
               } else {
@@ -764,11 +797,16 @@ bwd_dz_kernel(const DzArgs a) {
   const Operand opA1{a.w1 ? a.w1 : a.w, a.hdim, a.c0 + vt_begin * kLogitTileV, a.v, a.hdim};
   const Operand opB0{a.h0, a.hdim, n0, n_rows, a.hdim};
   const Operand opB1{a.h1 ? a.h1 : a.h0, a.hdim, n0, n_rows, a.hdim};
-  DzEpilogue<CAP, BIAS> epi{a, gs, nl, tgt, vt_begin, wm, half,
+  __shared__ __attribute__((aligned(16))) float rows[BIAS ? kRowDmaBytes / 4 : 4];
+  RowDma rd{};
+  if constexpr (BIAS)
+    rd = RowDma{dma_rsrc(a.bias, (int64_t)a.v * 4), lds_addr(reinterpret_cast<char*>(rows)),
+                a.c0 + vt_begin * kLogitTileV};
+  DzEpilogue<CAP, BIAS> epi{a, gs, nl, tgt, rows, vt_begin, wm, half,
                            __builtin_amdgcn_readfirstlane(n0 + wn * (kLogitTileN / 2))};
   LogitTile T;
-  T.run_stream<WSPLIT>(lds, opA0, opA1, opB0, opB1,
-                       logit_segments(a.h1 != nullptr, WSPLIT), a.hdim, ntiles, epi);
+  T.run_stream<WSPLIT, BIAS>(lds, opA0, opA1, opB0, opB1,
+                             logit_segments(a.h1 != nullptr, WSPLIT), a.hdim, ntiles, epi, rd);
 }
 
 // ------------------------------------------- contractions over a dz chunk

@@ -141,6 +141,34 @@ __device__ __forceinline__ void dma16_at(const u32x4& rs, uint32_t m0, uint32_t 
                "{m0}"(m0));
 }
 
+// 4 bytes per lane from global memory into LDS: lane l writes bytes
+// [4 l, 4 l + 4) of the 256-byte block at LDS byte address m0 (wave-uniform).
+// Same rules as dma16_at, with five wait states in front: the compiler does
+// not look inside the statement for hazards, and where it reloads the
+// descriptor from a spill lane (v_readlane, a VALU write of an SGPR) a vector
+// memory instruction must not read those SGPRs for five wait states.  (One
+// launch per tile, so the wait costs nothing measurable.)  The build scans the
+// assembly of every kernel for this hazard at the other LDS-DMA sites.
+__device__ __forceinline__ void dma4_at(const u32x4& rs, uint32_t m0, uint32_t off) {
+  asm volatile("s_nop 4\n\tbuffer_load_dword %0, %1, 0 offen lds" ::"v"(off), "s"(rs),
+               "{m0}"(m0));
+}
+
+// Per-row values of the A operand (an fp32 bias) for the epilogues of a
+// streamed tile sequence (Tile::run_stream with ROWS): each wave loads the 64
+// values of its half of a tile's 128 A rows (wave w: rows 64 (w % 2) + lane)
+// by LDS DMA together with the tile's first slice, into its own 256-byte
+// block of buffer t % 3.  Counted with that slice's loads, they have landed
+// when the tile's last slice has, and the buffer is not loaded again before
+// the tile's epilogue is done (the issue pointer runs two slices ahead).
+struct RowDma {
+  u32x4 rsrc;      // 4-byte values per A row; rows past its size read zero
+  uint32_t lds;    // LDS byte address of buffer 0 (kRowDmaBufs x 1 KB)
+  int row0;        // A row of the first tile
+};
+constexpr int kRowDmaBufs = 3;
+constexpr int kRowDmaBytes = kRowDmaBufs * 4 * 256;
+
 // LDS byte address of a pointer into the workgroup's LDS array.
 __device__ __forceinline__ uint32_t lds_addr(const char* p) {
   return __builtin_amdgcn_readfirstlane(
@@ -467,10 +495,12 @@ struct Tile {
   // Epi::kUsesLds asks for it (one extra barrier per tile), else null.  A2:
   // whether the second A operand is used at all (compile time; without it
   // sg.a must be 0 and a1_op is ignored, and the loop is the one-A loop).
-  template <bool A2, class Epi>
+  template <bool A2, bool ROWS, class Epi>
   __device__ __forceinline__ void run_stream(char* lds, const Operand a0_op, const Operand a1_op,
                                              const Operand b0_op, const Operand b1_op,
-                                             const SegPlan sg, int k_end, int ntiles, Epi& epi) {
+                                             const SegPlan sg, int k_end, int ntiles, Epi& epi,
+                                             const RowDma& rd = RowDma{}) {
+    static_assert(!ROWS || BM == 128, "row values: 64 rows per wave");
     const int kt_seg = (k_end + kBK - 1) / kBK;
     const int kt_tile = kt_seg * sg.n;
     if (kt_tile <= 0 || ntiles <= 0) return;
@@ -478,7 +508,7 @@ struct Tile {
     const typename SB::Src b1 = SB::source(sg.b ? b1_op : b0_op);
     const int past = sg.n * kt_seg;   // a slice index that reads zero in every segment
     // issue pointer: tile it, slice is, its A sources and ring stage
-    int it = 0, is = 0, islot = 0;
+    int it = 0, is = 0, islot = 0, ibuf = 0;
     Operand ao0 = a0_op, ao1 = a1_op;
     typename SA::Src a0 = SA::source(ao0);
     typename SA::Src a1 = a0;
@@ -488,6 +518,14 @@ struct Tile {
       const int seg = (kt >= kt_seg ? 1 : 0) + (sg.n > 2 && kt >= 2 * kt_seg ? 1 : 0);
       const int k0 = (kt - seg * kt_seg) * kBK;
       char* buf = lds + islot * kStage;
+      if constexpr (ROWS) {
+        if (is == 0 && it < ntiles) {
+          const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+          const int row = rd.row0 + it * BM + (wave & 1) * 64 + (int)(threadIdx.x & 63);
+          dma4_at(rd.rsrc, rd.lds + ibuf * 1024 + wave * 256, (uint32_t)row * 4);
+          ibuf = ibuf == kRowDmaBufs - 1 ? 0 : ibuf + 1;
+        }
+      }
       if constexpr (A2)
         SA::issue(((sg.a >> seg) & 1) ? a1 : a0, buf, k0);
       else

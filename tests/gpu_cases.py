@@ -120,6 +120,20 @@ def check_reduced(g: dict, o: dict, label: str = "") -> None:
     assert int(ri[1]) == int(g["hit"].numpy().astype(np.int64).sum()), f"{label} n_correct != sum hit"
 
 
+def check_vocab_grad_parts(a: np.ndarray, b: np.ndarray, targets: np.ndarray, vocab: int,
+                           name: str, label: str = "") -> None:
+    """grad_weight / grad_bias rows split in two, each within the tolerance on
+    its own: the rows that are some valid row's target (dominated by the
+    one-hot term) and the others (the softmax term alone, which the first
+    would otherwise outweigh at large vocabularies)."""
+    t = np.asarray(targets)
+    is_t = np.zeros(vocab, dtype=bool)
+    is_t[t[(t >= 0) & (t < vocab)]] = True
+    for sel, part in ((is_t, "target rows"), (~is_t, "softmax-only rows")):
+        if sel.any():
+            check_grad(a[sel], b[sel], f"{name} {part}", label)
+
+
 def check_grad(a: np.ndarray, b: np.ndarray, name: str, label: str = "") -> None:
     e = rel_fro(a, b)
     assert e <= TOL_GRAD, f"{label} {name}: relative Frobenius error {e}"

@@ -187,3 +187,21 @@ def test_noalloc_forward_rejects_oversized_problem():
     assert "16777216" in flce.flce_last_error()
     assert flce.flce_plan_info(flce.make_problem(2048, 640, 262144))["fwd_workspace_bytes"] \
         <= 16 << 20
+
+
+def test_lds_dma_hazard_scan():
+    """The build's scan of the kernel assembly flags an LDS-DMA load whose
+    descriptor an SGPR reload (v_readlane) wrote fewer than five wait states
+    before, and passes one with enough wait states or a scalar-written
+    descriptor."""
+    from linear_cross_entropy_fp32_amd.build import lds_dma_hazards
+    bad = ("_Zk:\n\tv_readlane_b32 s11, v251, 16\n\ts_nop 0\n"
+           "\tbuffer_load_dword v1, s[8:11], 0 offen lds\n")
+    ok1 = ("_Zk:\n\tv_readlane_b32 s11, v251, 16\n\ts_nop 4\n"
+           "\tbuffer_load_dword v1, s[8:11], 0 offen lds\n")
+    ok2 = ("_Zk:\n\ts_mov_b32 s11, 0x20000\n\ts_nop 0\n"
+           "\tbuffer_load_dwordx4 v1, s[8:11], 0 offen lds\n")
+    m0 = "_Zk:\n\ts_mov_b32 m0, s4\n\tbuffer_load_dwordx4 v1, s[8:11], 0 offen lds\n"
+    assert len(lds_dma_hazards(bad)) == 1
+    assert lds_dma_hazards(ok1) == [] and lds_dma_hazards(ok2) == []
+    assert len(lds_dma_hazards(m0)) == 1

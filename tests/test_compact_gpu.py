@@ -14,7 +14,7 @@ import linear_cross_entropy_fp32_amd as flce
 from linear_cross_entropy_fp32_amd import _binding, synth
 from oracle import backward, forward
 from tests.gpu_cases import (check_compact_tokens, check_fullsize_grads, check_grad,
-                             check_reduced, prob_of, rel_fro,
+                             check_reduced, check_vocab_grad_parts, prob_of, rel_fro,
                              run_gpu, say, to_f64)
 
 pytestmark = pytest.mark.gpu
@@ -69,8 +69,12 @@ def test_compact_parity(w):
     check_reduced(g, o, label=w.name)
     check_grad(g["grad_hidden"].numpy(), og["grad_hidden"], "grad_hidden", w.name)
     check_grad(g["grad_weight"].numpy(), og["grad_weight"], "grad_weight", w.name)
+    check_vocab_grad_parts(g["grad_weight"].numpy(), og["grad_weight"], inp.targets.numpy(),
+                           w.vocab, "grad_weight", w.name)
     if inp.bias is not None:
         check_grad(g["grad_bias"].numpy(), og["grad_bias"], "grad_bias", w.name)
+        check_vocab_grad_parts(g["grad_bias"].numpy(), og["grad_bias"], inp.targets.numpy(),
+                               w.vocab, "grad_bias", w.name)
     if not valid.any():
         for k in ("grad_hidden", "grad_weight"):
             assert torch.count_nonzero(g[k]).item() == 0, k

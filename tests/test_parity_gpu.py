@@ -8,8 +8,8 @@ import torch
 import linear_cross_entropy_fp32_amd as flce
 from linear_cross_entropy_fp32_amd import synth
 from oracle import Problem, backward, final_logits, forward
-from tests.gpu_cases import (check_fullsize, check_grad, check_reduced, check_tokens, prob_of,
-                             rel_fro, run_gpu,
+from tests.gpu_cases import (check_fullsize, check_grad, check_reduced, check_tokens,
+                             check_vocab_grad_parts, prob_of, rel_fro, run_gpu,
                              say, to_f64)
 
 pytestmark = pytest.mark.gpu
@@ -72,8 +72,12 @@ def test_small_parity(w):
     check_reduced(g, o, label=w.name)
     check_grad(g["grad_hidden"].numpy(), og["grad_hidden"], "grad_hidden", w.name)
     check_grad(g["grad_weight"].numpy(), og["grad_weight"], "grad_weight", w.name)
+    check_vocab_grad_parts(g["grad_weight"].numpy(), og["grad_weight"], inp.targets.numpy(),
+                           w.vocab, "grad_weight", w.name)
     if inp.bias is not None:
         check_grad(g["grad_bias"].numpy(), og["grad_bias"], "grad_bias", w.name)
+        check_vocab_grad_parts(g["grad_bias"].numpy(), og["grad_bias"], inp.targets.numpy(),
+                               w.vocab, "grad_bias", w.name)
 
 
 def test_lm_head_over_2gib():
