@@ -154,3 +154,65 @@ def test_mutation_is_caught(name, monkeypatch):
         except (AssertionError, ValueError, IndexError):
             caught += 1
     assert caught > 0, f"mutation {name} passed every pin"
+
+
+# ------------------------------------------- standalone cross-entropy oracle
+import oracle.ce_oracle as ceo  # noqa: E402
+import tests.test_ce_oracle_pins as cepins  # noqa: E402
+
+CE_PINS = [(cepins.test_against_torch, dict(reduction=r)) for r in ("none", "mean", "sum")] + [
+    (cepins.test_closed_forms, {}), (cepins.test_invariants_and_reductions, {})]
+_ce_forward_orig = ceo.ce_forward
+_ce_scale_orig = ceo.ce_row_scale
+
+
+def _ce_no_onehot(logits, targets, ignore_index=-100, mean_divisor=0.0):
+    f = _ce_forward_orig(logits, targets, ignore_index, mean_divisor)
+    f["grad"] = np.where(f["valid"][:, None], np.exp(np.asarray(logits) - f["lse"][:, None]), 0.0)
+    return f
+
+
+def _ce_ignored_rows_keep_grad(logits, targets, ignore_index=-100, mean_divisor=0.0):
+    f = _ce_forward_orig(logits, targets, ignore_index, mean_divisor)
+    f["grad"] = f["grad"] + np.where(f["valid"][:, None], 0.0,
+                                     np.exp(np.asarray(logits) - f["lse"][:, None]))
+    return f
+
+
+def _ce_mean_over_all_rows(targets, vocab, mode, grad_out, ignore_index=-100, mean_divisor=0.0):
+    out = _ce_scale_orig(targets, vocab, mode, grad_out, ignore_index, mean_divisor)
+    if mode == "mean":
+        nv = int(ceo.ce_valid(targets, vocab, ignore_index)[0].sum())
+        out = out * nv / len(targets)
+    return out
+
+
+def _ce_loss_sign(logits, targets, ignore_index=-100, mean_divisor=0.0):
+    f = _ce_forward_orig(logits, targets, ignore_index, mean_divisor)
+    f["loss"] = -f["loss"]
+    f["loss_sum"] = -f["loss_sum"]
+    f["loss_mean"] = -f["loss_mean"]
+    return f
+
+
+CE_MUTATIONS = {
+    "ce_no_onehot": ("ce_forward", _ce_no_onehot),
+    "ce_ignored_rows_keep_grad": ("ce_forward", _ce_ignored_rows_keep_grad),
+    "ce_mean_over_all_rows": ("ce_row_scale", _ce_mean_over_all_rows),
+    "ce_loss_sign": ("ce_forward", _ce_loss_sign),
+}
+
+
+@pytest.mark.parametrize("name", sorted(CE_MUTATIONS))
+def test_ce_mutation_is_caught(name, monkeypatch):
+    attr, fn = CE_MUTATIONS[name]
+    monkeypatch.setattr(ceo, attr, fn)
+    for mod_name in ("ce_forward", "ce_backward"):
+        monkeypatch.setattr(cepins, mod_name, getattr(ceo, mod_name))
+    caught = 0
+    for test, kw in CE_PINS:
+        try:
+            test(**kw)
+        except (AssertionError, ValueError, IndexError):
+            caught += 1
+    assert caught > 0, f"mutation {name} passed every pin"
