@@ -474,6 +474,68 @@ def per_config(args, hip) -> dict:
     return out
 
 
+# The Liger-Kernel page's in-place "none+weighted" fwd+bwd figures (ms, 8192
+# rows, bf16): context for the materialised-logit cross-entropy, not a target.
+PAGES_CE_MS = {32000: {"H100": 1.298, "B300": 0.65}, 128256: {"H100": 4.803, "B300": 2.25},
+               151936: {"H100": 5.807, "B300": 2.70}}
+
+
+def materialised_ce(args, hip) -> dict:
+    """The standalone cross-entropy on materialised logits (flce_ce_forward with
+    the gradient written in place, then flce_ce_backward scaling it by
+    per-row weights), 8192 bf16 rows per vocabulary of the Liger-Kernel
+    page's benchmark.  Each step restores the logits and evicts L2 and MALL
+    outside its events.  HBM bytes per step (algorithmic): the forward reads
+    and writes every element once, the backward reads and writes it once:
+    4 * N * V * 2 bytes."""
+    import torch
+
+    import linear_cross_entropy_fp32_amd as flce
+    from linear_cross_entropy_fp32_amd import synth
+    out = {}
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+    for name, (n, v) in synth.CE_WORKLOADS.items():
+        pristine, targets, weights = synth.ce_inputs(n, v, 4242, "bf16", device="cuda:0")
+        x = torch.empty_like(pristine)
+        t, w = targets.to(dev), weights.to(dev)
+        steps = max(3, args.per_config_steps)
+        ev = Events(hip, 3 * steps)
+        for i in range(steps + 2):        # two untimed warmup steps
+            x.copy_(pristine)
+            flush.fill_(i & 255)
+            k = i - 2
+            if k >= 0:
+                _hip_ok(hip.hipEventRecord(ctypes.c_void_p(ev[3 * k]), sp))
+            f = flce.flce_ce_forward(x, t)
+            if k >= 0:
+                _hip_ok(hip.hipEventRecord(ctypes.c_void_p(ev[3 * k + 1]), sp))
+            flce.flce_ce_backward(x, t, f["reduced_i64"], flce.FLCE_GRAD_PER_TOKEN, w)
+            if k >= 0:
+                _hip_ok(hip.hipEventRecord(ctypes.c_void_p(ev[3 * k + 2]), sp))
+        torch.cuda.synchronize()
+        fwd = [ev.ms(3 * k, 3 * k + 1) for k in range(steps)]
+        bwd = [ev.ms(3 * k + 1, 3 * k + 2) for k in range(steps)]
+        ev.close()
+        fm, bm = pct(fwd, 50), pct(bwd, 50)
+        nbytes = n * v * 2
+        out[name] = {"n_rows": n, "vocab": v, "dtype": "bf16", "usage": "none+weighted, in place",
+                     "fwd_ms": fm, "bwd_ms": bm, "ms": fm + bm,
+                     "fwd_gbs": 2 * nbytes / (fm * 1e-3) / 1e9,
+                     "bwd_gbs": 2 * nbytes / (bm * 1e-3) / 1e9,
+                     "hbm_frac": 4 * nbytes / ((fm + bm) * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                     "row_held_in_registers": (v * 2) % 16 == 0 and v * 2 <= 1024 * 20 * 16,
+                     "pages_ms": PAGES_CE_MS.get(v)}
+        print(f"bench.py: materialised_ce {name}: fwd {fm:.3f} ms, bwd {bm:.3f} ms",
+              file=sys.stderr, flush=True)
+        del pristine, x
+        torch.cuda.empty_cache()
+    del flush
+    return out
+
+
 def main() -> int:
     args = parse()
     if args.traffic_record:
@@ -549,6 +611,7 @@ def main() -> int:
         out["cpu_baseline"] = cpu_baseline(w, synth.make_inputs(w), args.cpu_seconds)
     if args.per_config_steps > 0 and not args.compact:
         out["per_config"] = per_config(args, hip)
+        out["materialised_ce"] = materialised_ce(args, hip)
     print(json.dumps(out), flush=True)
     return 0
 

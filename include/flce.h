@@ -190,6 +190,49 @@ int flce_backward(const flce_problem* p, const void* hidden, const void* weight,
 #define FLCE_KERNEL_CONTRACT 2
 int flce_set_timing_events(int kernel, void* const* events, int n_pairs);
 
+/* ------------------------------------------------------------------------
+ * Standalone cross-entropy on materialised logits (Liger-Kernel pull request
+ * 1574, "Summary" items 1 and 2): for logits that are already in memory, the
+ * per-token loss lse_n - z[n, t_n] in fp32, its reductions, and the gradient
+ * with respect to the logits written in place of them, which the backward
+ * scales row by row in place (one fp32 multiply and one rounding per
+ * element: no (rows x vocabulary) temporary, no device-to-host sync).
+ * The z_loss the page mentions has no formula on it and is not provided.
+ */
+typedef struct flce_ce_problem {
+  int64_t n_rows;        /* N >= 0 rows of logits / targets                      */
+  int64_t vocab;         /* V >= 1 logits per row; V * element size < 2^31       */
+  int32_t logits_dtype;  /* FLCE_BF16 or FLCE_F32: logits and the gradient        */
+  int32_t reserved;      /* must be 0                                            */
+  int64_t ignore_index;  /* usually -100                                         */
+  float mean_divisor;    /* > 0: the mean divides by it, else by n_valid          */
+  int32_t reserved2;     /* must be 0                                            */
+} flce_ce_problem;
+
+/* Forward.  logits [N, V] (dtype per p->logits_dtype, 16-byte aligned) is read;
+ * with grad_in_place = 1 each row is then overwritten with
+ * softmax(z_n) - onehot(t_n) in the same dtype (a zero row for a row that
+ * carries no loss): the gradient of sum_n loss_n, which flce_ce_backward
+ * scales.  targets [N] int64 (ignore_index marks ignored rows; other values
+ * outside [0, V) are ignored and counted in reduced_i64[1]).
+ * Outputs (device, fp32 unless noted): loss [N] (0 on ignored rows), lse [N],
+ * reduced_f32 [2]: loss_sum, loss_mean; reduced_i64 [2]: n_valid, n_bad.
+ * No workspace.  Errors as for flce_forward (FLCE_ERR_* before any launch). */
+int flce_ce_forward(const flce_ce_problem* p, void* logits, const int64_t* targets,
+                    float* loss, float* lse, float* reduced_f32, int64_t* reduced_i64,
+                    int grad_in_place, void* stream);
+
+/* Backward, in place: grad_logits [N, V] (the forward's in-place output) row n
+ * is multiplied by g_n in fp32 and rounded once to the logits dtype, with
+ * g_n = grad_out[0] / divisor (FLCE_GRAD_MEAN; divisor = mean_divisor if > 0,
+ * else n_valid from reduced_i64, read on the device), grad_out[0]
+ * (FLCE_GRAD_SUM) or grad_out[n] (FLCE_GRAD_PER_TOKEN, reduction "none"
+ * with any per-row weights); rows that carry no loss are set to 0.  The
+ * stored gradient is consumed: a second call scales it again. */
+int flce_ce_backward(const flce_ce_problem* p, void* grad_logits, const int64_t* targets,
+                     const int64_t* reduced_i64, int grad_mode, const float* grad_out,
+                     void* stream);
+
 /* How the library tiles a problem (support; nothing is launched, no HIP
  * call).  Writes min(n_out, FLCE_PLAN_FIELDS) values to out (host memory), in
  * this order, and returns that count, or a negative FLCE_ERR_* code for an

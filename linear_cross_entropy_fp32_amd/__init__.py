@@ -12,3 +12,5 @@ from ._binding import (FLCE_BF16, FLCE_F32, FLCE_GRAD_MEAN, FLCE_GRAD_PER_TOKEN,
                        flce_last_error, flce_plan_info, flce_set_timing_events, flce_validate,
                        flce_workspace_bytes, lib,
                        linear_cross_entropy, make_problem)
+from ._binding import (FlceCeProblem, cross_entropy, flce_ce_backward,  # noqa: F401,E402
+                       flce_ce_forward)

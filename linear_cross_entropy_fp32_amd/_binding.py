@@ -23,7 +23,7 @@ ERROR_NAMES = {-1: "FLCE_ERR_NULL", -2: "FLCE_ERR_SHAPE", -3: "FLCE_ERR_DTYPE",
                -7: "FLCE_ERR_ARG"}
 EXPORTED = ("flce_validate", "flce_workspace_bytes", "flce_forward", "flce_backward",
             "flce_last_error", "flce_abi_version", "flce_set_timing_events", "flce_plan_info",
-            "flce_forward_noalloc")
+            "flce_forward_noalloc", "flce_ce_forward", "flce_ce_backward")
 PLAN_FIELDS = ("chunk_rows", "n_chunks", "fwd_splits", "fwd_tiles_per_split",
                "dz_tiles_per_wg", "gh_splits", "gh_rows_per_split", "window_token_tiles",
                "token_tile_fastest", "fwd_workspace_bytes", "bwd_workspace_bytes",
@@ -38,6 +38,14 @@ class FlceProblem(ctypes.Structure):
                 ("weight_dtype", ctypes.c_int32), ("logit_scale", ctypes.c_float),
                 ("softcap", ctypes.c_float), ("ignore_index", ctypes.c_int64),
                 ("mean_divisor", ctypes.c_float), ("compact_valid", ctypes.c_int32)]
+
+
+class FlceCeProblem(ctypes.Structure):
+    """Mirror of ``flce_ce_problem`` in include/flce.h."""
+    _fields_ = [("n_rows", ctypes.c_int64), ("vocab", ctypes.c_int64),
+                ("logits_dtype", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("ignore_index", ctypes.c_int64), ("mean_divisor", ctypes.c_float),
+                ("reserved2", ctypes.c_int32)]
 
 
 class FlceError(RuntimeError):
@@ -78,6 +86,11 @@ def lib() -> ctypes.CDLL:
         L.flce_abi_version.restype = ctypes.c_int
         L.flce_set_timing_events.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_int]
         L.flce_set_timing_events.restype = ctypes.c_int
+        cp = ctypes.POINTER(FlceCeProblem)
+        L.flce_ce_forward.argtypes = [cp, vp, i64p, f32p, f32p, f32p, i64p, ctypes.c_int, vp]
+        L.flce_ce_forward.restype = ctypes.c_int
+        L.flce_ce_backward.argtypes = [cp, vp, i64p, i64p, ctypes.c_int, f32p, vp]
+        L.flce_ce_backward.restype = ctypes.c_int
         L.flce_plan_info.argtypes = [pp, ctypes.POINTER(ctypes.c_int64), ctypes.c_int]
         L.flce_plan_info.restype = ctypes.c_int
         if L.flce_abi_version() != 1:
@@ -333,3 +346,99 @@ def linear_cross_entropy(hidden: torch.Tensor, weight: torch.Tensor, targets: to
         raise ValueError(f"reduction must be one of {sorted(_MODES)}")
     return _LinearCrossEntropy.apply(hidden, weight, bias, targets, logit_scale, softcap,
                                      reduction, num_items, ignore_index, bool(compact_valid))
+
+
+# ------------------------------------- cross-entropy on materialised logits
+
+def ce_problem_for(logits: torch.Tensor, ignore_index: int = -100,
+                   mean_divisor: float = 0.0) -> FlceCeProblem:
+    if logits.dim() != 2:
+        raise ValueError(f"logits must be [N, V], got {tuple(logits.shape)}")
+    return FlceCeProblem(logits.shape[0], logits.shape[1], _dtype_code(logits), 0,
+                         int(ignore_index), float(mean_divisor), 0)
+
+
+def flce_ce_forward(logits: torch.Tensor, targets: torch.Tensor, ignore_index: int = -100,
+                    mean_divisor: float = 0.0, grad_in_place: bool = True) -> dict:
+    """Run ``flce_ce_forward`` on the current stream.  With grad_in_place the
+    logits tensor is overwritten with softmax - onehot per row.  Returns
+    device tensors loss, lse [N] f32, reduced_f32 [2] (loss_sum, loss_mean),
+    reduced_i64 [2] (n_valid, n_bad)."""
+    if targets is None:
+        raise ValueError("targets are required")
+    dev = logits.device
+    for t, nm in ((logits, "logits"), (targets, "targets")):
+        _require(t, nm, dev)
+    if targets.dtype != torch.int64 or targets.shape != (logits.shape[0],):
+        raise ValueError("targets must be int64 [N]")
+    prob = ce_problem_for(logits, ignore_index, mean_divisor)
+    n = logits.shape[0]
+    f32 = dict(dtype=torch.float32, device=dev)
+    out = dict(loss=torch.empty(n, **f32), lse=torch.empty(n, **f32),
+               reduced_f32=torch.empty(2, **f32),
+               reduced_i64=torch.empty(2, dtype=torch.int64, device=dev))
+    _check(lib().flce_ce_forward(ctypes.byref(prob), _ptr(logits), _ptr(targets),
+                                 _ptr(out["loss"]), _ptr(out["lse"]), _ptr(out["reduced_f32"]),
+                                 _ptr(out["reduced_i64"]), 1 if grad_in_place else 0,
+                                 _stream(dev)))
+    return out
+
+
+def flce_ce_backward(grad_logits: torch.Tensor, targets: torch.Tensor,
+                     reduced_i64: torch.Tensor, grad_mode: int, grad_out: torch.Tensor,
+                     ignore_index: int = -100, mean_divisor: float = 0.0) -> torch.Tensor:
+    """Run ``flce_ce_backward``: scales grad_logits (the forward's in-place
+    output) row by row in place and returns it."""
+    dev = grad_logits.device
+    for t, nm in ((grad_logits, "grad_logits"), (targets, "targets"),
+                  (reduced_i64, "reduced_i64"), (grad_out, "grad_out")):
+        _require(t, nm, dev)
+    if grad_out.dtype != torch.float32:
+        raise ValueError("grad_out must be float32")
+    prob = ce_problem_for(grad_logits, ignore_index, mean_divisor)
+    _check(lib().flce_ce_backward(ctypes.byref(prob), _ptr(grad_logits), _ptr(targets),
+                                  _ptr(reduced_i64), int(grad_mode), _ptr(grad_out),
+                                  _stream(dev)))
+    return grad_logits
+
+
+class _CrossEntropyInPlace(torch.autograd.Function):
+    """Cross-entropy on materialised logits whose forward writes the gradient
+    in place of the logits and whose backward scales it in place: the graph
+    can be backpropagated once."""
+
+    @staticmethod
+    def forward(ctx, logits, targets, reduction, num_items, ignore_index):
+        mean_div = float(num_items) if num_items else 0.0
+        out = flce_ce_forward(logits, targets, ignore_index, mean_div, grad_in_place=True)
+        ctx.save_for_backward(logits, targets, out["reduced_i64"])
+        ctx.cfg = (reduction, mean_div, ignore_index)
+        ctx.mark_non_differentiable(out["reduced_i64"])
+        if reduction == "none":
+            loss = out["loss"]
+        elif reduction == "sum":
+            loss = out["reduced_f32"][0]
+        else:
+            loss = out["reduced_f32"][1]
+        return loss, out["reduced_i64"][0]
+
+    @staticmethod
+    def backward(ctx, g_loss, _g_nv):
+        logits, targets, red_i64 = ctx.saved_tensors
+        reduction, mean_div, ignore_index = ctx.cfg
+        g = g_loss.to(torch.float32).contiguous().reshape(-1)
+        flce_ce_backward(logits, targets, red_i64, _MODES[reduction], g, ignore_index, mean_div)
+        return logits, None, None, None, None
+
+
+def cross_entropy(logits: torch.Tensor, targets: torch.Tensor, reduction: str = "mean",
+                  num_items: Optional[float] = None, ignore_index: int = -100):
+    """Cross-entropy on [N, V] logits (bf16 or fp32) with fp32 per-token
+    losses; the gradient is written in place of the logits (which must be a
+    leaf tensor the caller does not need afterwards).  Returns
+    (loss, n_valid)."""
+    if targets is None:
+        raise ValueError("targets must be provided")
+    if reduction not in _MODES:
+        raise ValueError(f"reduction must be one of {sorted(_MODES)}")
+    return _CrossEntropyInPlace.apply(logits, targets, reduction, num_items, ignore_index)

@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG_DIR)
 CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG_DIR, "libflce.so")
-SOURCES = ["flce_kernels.hip", "flce_api.cpp"]
+SOURCES = ["flce_kernels.hip", "ce_kernels.hip", "flce_api.cpp"]
 ARCH = "gfx950"
 
 # Packed fp32 VALU forms are kept off: hipcc would otherwise fuse pairs of

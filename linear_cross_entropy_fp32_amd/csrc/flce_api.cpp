@@ -9,6 +9,7 @@
 #include <cstring>
 #include <mutex>
 
+#include "ce_internal.h"
 #include "flce.h"
 #include "flce_internal.h"
 
@@ -394,6 +395,83 @@ int flce_set_timing_events(int kernel, void* const* events, int n_pairs) {
 }
 
 const char* flce_last_error(void) { return g_err; }
+
+static int ce_validate(const flce_ce_problem* p) {
+  if (!p) return fail(FLCE_ERR_NULL, "problem is NULL");
+  if (p->reserved != 0 || p->reserved2 != 0)
+    return fail(FLCE_ERR_ARG, "flce_ce_problem reserved fields must be 0");
+  if (p->logits_dtype != FLCE_BF16 && p->logits_dtype != FLCE_F32)
+    return fail(FLCE_ERR_DTYPE, "logits_dtype=%d unsupported (bf16 or fp32)", p->logits_dtype);
+  const int64_t elem = p->logits_dtype == FLCE_F32 ? 4 : 2;
+  if (p->n_rows < 0 || p->n_rows > (int64_t(1) << 31) - 1)
+    return fail(FLCE_ERR_SHAPE, "n_rows=%lld out of range [0, 2^31)", (long long)p->n_rows);
+  if (p->vocab < 1 || p->vocab * elem > (int64_t(1) << 31) - 1)
+    return fail(FLCE_ERR_SHAPE, "vocab=%lld out of range (a row must stay below 2^31 bytes)",
+                (long long)p->vocab);
+  if (std::isnan(p->mean_divisor) || std::isinf(p->mean_divisor))
+    return fail(FLCE_ERR_ARG, "mean_divisor must be finite");
+  return FLCE_OK;
+}
+
+int flce_ce_forward(const flce_ce_problem* p, void* logits, const int64_t* targets, float* loss,
+                    float* lse, float* reduced_f32, int64_t* reduced_i64, int grad_in_place,
+                    void* stream) {
+  g_err[0] = 0;
+  int rc = ce_validate(p);
+  if (rc) return rc;
+  if (grad_in_place != 0 && grad_in_place != 1)
+    return fail(FLCE_ERR_ARG, "grad_in_place must be 0 or 1");
+  if (!reduced_f32 || !reduced_i64) return fail(FLCE_ERR_NULL, "reduced outputs are required");
+  if (p->n_rows > 0 && (!logits || !targets || !loss || !lse))
+    return fail(FLCE_ERR_NULL, "logits, targets, loss and lse are required");
+  if ((logits && !aligned(logits, 16)) || (targets && !aligned(targets, 8)) ||
+      (loss && !aligned(loss, 4)) || (lse && !aligned(lse, 4)) || !aligned(reduced_f32, 4) ||
+      !aligned(reduced_i64, 8))
+    return fail(FLCE_ERR_ALIGN, "logits must be 16-byte aligned, the others per dtype");
+  CeArgs a{};
+  a.logits = logits;
+  a.grad = logits;
+  a.tgt = targets;
+  a.loss = loss;
+  a.lse = lse;
+  a.n = p->n_rows;
+  a.v = p->vocab;
+  a.ignore_index = p->ignore_index;
+  a.grad_in_place = grad_in_place;
+  return hip_check(launch_ce_forward(a, p->logits_dtype == FLCE_F32,
+                                     p->mean_divisor > 0 ? p->mean_divisor : 0.f, reduced_f32,
+                                     reduced_i64, reinterpret_cast<hipStream_t>(stream)),
+                   "ce_forward");
+}
+
+int flce_ce_backward(const flce_ce_problem* p, void* grad_logits, const int64_t* targets,
+                     const int64_t* reduced_i64, int grad_mode, const float* grad_out,
+                     void* stream) {
+  g_err[0] = 0;
+  int rc = ce_validate(p);
+  if (rc) return rc;
+  if (grad_mode < FLCE_GRAD_MEAN || grad_mode > FLCE_GRAD_PER_TOKEN)
+    return fail(FLCE_ERR_ARG, "grad_mode=%d invalid", grad_mode);
+  if (!grad_out || !reduced_i64) return fail(FLCE_ERR_NULL, "grad_out and reduced_i64 are required");
+  if (p->n_rows > 0 && (!grad_logits || !targets))
+    return fail(FLCE_ERR_NULL, "grad_logits and targets are required");
+  if ((grad_logits && !aligned(grad_logits, 16)) || (targets && !aligned(targets, 8)) ||
+      !aligned(reduced_i64, 8) || !aligned(grad_out, 4))
+    return fail(FLCE_ERR_ALIGN, "grad_logits must be 16-byte aligned, the others per dtype");
+  CeBwdArgs a{};
+  a.grad = grad_logits;
+  a.tgt = targets;
+  a.red_i64 = reduced_i64;
+  a.grad_out = grad_out;
+  a.n = p->n_rows;
+  a.v = p->vocab;
+  a.ignore_index = p->ignore_index;
+  a.mode = grad_mode;
+  a.mean_divisor = p->mean_divisor > 0 ? p->mean_divisor : 0.f;
+  return hip_check(launch_ce_backward(a, p->logits_dtype == FLCE_F32,
+                                      reinterpret_cast<hipStream_t>(stream)),
+                   "ce_backward");
+}
 
 int flce_plan_info(const flce_problem* p, int64_t* out, int n_out) {
   g_err[0] = 0;

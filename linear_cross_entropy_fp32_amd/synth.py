@@ -163,3 +163,30 @@ def input_checksum(inp: Inputs) -> str:
             t = t.view(torch.int16)
         hsh.update(t.numpy().tobytes())
     return hsh.hexdigest()[:32]
+
+
+# ------------------------------------------- materialised-logit workloads
+# The Liger-Kernel pull request's benchmark ("Details"): 8192 rows, random
+# logits, targets uniform with every 17th ignored, vocabularies 32000, 128256
+# and 151936; here logits ~ N(0, 1) in bf16 (the page's "random logits"), and
+# per-row weights ~ U[0, 2) for its "none+weighted" usage.
+CE_WORKLOADS = {f"ce_{v}": (8192, v) for v in (32000, 128256, 151936)}
+
+
+def ce_inputs(n: int, v: int, seed: int, dtype: str = "bf16", device: str = "cpu",
+              ignore_every: int = 17):
+    """(logits [n, v], targets [n] int64, weights [n] f32) drawn from one
+    generator on `device` (logits) and one CPU generator (targets, weights),
+    both seeded with `seed`."""
+    g = torch.Generator(device=device).manual_seed(seed)
+    logits = torch.randn(n, v, generator=g, dtype=torch.float32, device=device)
+    if dtype == "bf16":
+        logits = logits.to(torch.bfloat16)
+    elif dtype != "f32":
+        raise ValueError(dtype)
+    gc = torch.Generator().manual_seed(seed + 1)
+    targets = torch.randint(0, v, (n,), generator=gc, dtype=torch.int64)
+    if ignore_every > 0:
+        targets[::ignore_every] = IGNORE_INDEX
+    weights = torch.rand(n, generator=gc, dtype=torch.float32) * 2.0
+    return logits, targets, weights

@@ -72,9 +72,9 @@ def ce_row_scale(targets: np.ndarray, vocab: int, mode: str, grad_out,
     g = np.asarray(grad_out, dtype=np.float64)
     if mode == "mean":
         divisor = mean_divisor if mean_divisor > 0 else float(valid.sum())
-        gn = np.full(len(valid), float(g) / divisor if divisor > 0 else 0.0)
+        gn = np.full(len(valid), float(g.reshape(-1)[0]) / divisor if divisor > 0 else 0.0)
     elif mode == "sum":
-        gn = np.full(len(valid), float(g))
+        gn = np.full(len(valid), float(g.reshape(-1)[0]))
     elif mode == "none":
         gn = g.reshape(-1).copy()
     else:

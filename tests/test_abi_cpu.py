@@ -33,21 +33,22 @@ def test_library_exports_every_declared_symbol():
         assert re.search(rf"\bT {name}$", out, flags=re.M), f"{name} missing from dynamic symbols"
 
 
-def test_struct_layout_matches_header(tmp_path):
+@pytest.mark.parametrize("struct,cname", [(_binding.FlceProblem, "flce_problem"),
+                                          (_binding.FlceCeProblem, "flce_ce_problem")])
+def test_struct_layout_matches_header(tmp_path, struct, cname):
     src = tmp_path / "layout.c"
-    fields = [f for f, _ in _binding.FlceProblem._fields_]
+    fields = [f for f, _ in struct._fields_]
     fmt = " ".join(["%zu"] * (len(fields) + 1))
-    offs = "".join(f", offsetof(flce_problem, {f})" for f in fields)
+    offs = "".join(f", offsetof({cname}, {f})" for f in fields)
     src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "flce.h"\n'
-                   f'int main(void) {{ printf("{fmt}\\n", sizeof(flce_problem){offs}); '
+                   f'int main(void) {{ printf("{fmt}\\n", sizeof({cname}){offs}); '
                    'return 0; }\n')
     exe = tmp_path / "layout"
     subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)],
                    check=True)
     vals = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True,
                                            check=True).stdout.split()]
-    expect = [ctypes.sizeof(_binding.FlceProblem)] + [
-        getattr(_binding.FlceProblem, f).offset for f, _ in _binding.FlceProblem._fields_]
+    expect = [ctypes.sizeof(struct)] + [getattr(struct, f).offset for f, _ in struct._fields_]
     assert vals == expect
 
 
@@ -205,3 +206,28 @@ def test_lds_dma_hazard_scan():
     assert len(lds_dma_hazards(bad)) == 1
     assert lds_dma_hazards(ok1) == [] and lds_dma_hazards(ok2) == []
     assert len(lds_dma_hazards(m0)) == 1
+
+
+def test_ce_entry_points_reject_before_launch():
+    """The cross-entropy entry points check the problem and the pointers
+    before anything is launched (fake pointers, never dereferenced)."""
+    lib = flce.lib()
+    A = _fake(0x100000)
+    P = lambda **kw: ctypes.byref(_binding.FlceCeProblem(**dict(
+        dict(n_rows=8, vocab=100, logits_dtype=0, reserved=0, ignore_index=-100,
+             mean_divisor=0.0, reserved2=0), **kw)))
+    fwd = lambda p, logits=A, inplace=1: lib.flce_ce_forward(p, logits, A, A, A, A, A, inplace,
+                                                              None)
+    assert fwd(P(vocab=0)) == -2
+    assert fwd(P(n_rows=-1)) == -2
+    assert fwd(P(vocab=1 << 30, logits_dtype=1)) == -2      # a row of 4 GiB
+    assert fwd(P(logits_dtype=5)) == -3
+    assert fwd(P(reserved=1)) == -7
+    assert fwd(P(mean_divisor=float("nan"))) == -7
+    assert fwd(P(), inplace=2) == -7
+    assert fwd(P(), logits=None) == -1
+    assert fwd(P(), logits=_fake(0x100008)) == -4
+    bwd = lambda p, mode=0: lib.flce_ce_backward(p, A, A, A, mode, A, None)
+    assert bwd(P(), mode=3) == -7
+    assert bwd(P(vocab=0)) == -2
+    assert lib.flce_ce_backward(P(), A, A, A, 0, None, None) == -1
