@@ -57,6 +57,9 @@ def parse():
                          "--pmc FETCH_SIZE / WRITE_SIZE output directories of a bench run and of "
                          "a --copy-calibration-mib run (no GPU needed)")
     ap.add_argument("--traffic-kernel", default="contract_kernel")
+    ap.add_argument("--ce-only", action="store_true",
+                    help="only measure the standalone cross-entropy on materialised logits "
+                         "(the materialised_ce record) and print it")
     ap.add_argument("--library-gemm", action="store_true",
                     help="only time the vendor GEMM library (torch.mm, hipBLASLt) on the plain "
                          "products of the workload's step, as a reference for what a bf16 GEMM "
@@ -561,8 +564,11 @@ def main() -> int:
         return 0
 
     from linear_cross_entropy_fp32_amd import synth
-    w = synth.WORKLOADS[args.workload]
     hip = _hip_runtime()
+    if args.ce_only:
+        print(json.dumps({"materialised_ce": materialised_ce(args, hip)}), flush=True)
+        return 0
+    w = synth.WORKLOADS[args.workload]
     r = Runner(w, args.compact)
     m = measure(r, args.steps, args.warmup, hip, kernel_events=True)
     n, hd, v = w.n_tokens, w.hidden, w.vocab
