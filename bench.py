@@ -303,8 +303,9 @@ class Runner:
         self.t = inp.targets.to(dev)
         self.go = inp.grad_out.to(dev).reshape(-1)
         n, hd, v = w.n_tokens, w.hidden, w.vocab
+        # the backward reuses what the forward prepared in the same workspace
         self.prob = _binding.problem_for(self.h, self.wt, w.logit_scale, w.softcap,
-                                         compact_valid=compact)
+                                         compact_valid=compact, reuse_prepared=True)
         self.ws_bytes = flce.flce_workspace_bytes(self.prob)
         self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=dev)
         f32 = dict(dtype=torch.float32, device=dev)

@@ -64,11 +64,13 @@ typedef struct flce_problem {
   int64_t vocab;         /* V >= 1 rows of weight                                 */
   int32_t hidden_dtype;  /* FLCE_BF16 or FLCE_F32 (fp32 hidden states)            */
   int32_t weight_dtype;  /* FLCE_BF16, or FLCE_F32 (an fp32 lm_head, e.g. an fp32
-                            master weight: it is split on the device into bf16
-                            high and low parts, and the logits take
-                            W_hi.h + W_lo.h, plus W_hi.h_lo with fp32 hidden,
-                            which keeps them at fp32 accuracy; grad_hidden
-                            takes W_hi.  The split needs 4*V*H workspace bytes.) */
+                            master weight).  An fp32 operand (lm_head or hidden)
+                            enters the MFMA products rounded to bf16 on the
+                            device (2*V*H or 2*N*H workspace bytes), and the
+                            target logit, which the loss takes directly, is
+                            computed from the unrounded operands, so the
+                            per-token loss stays within ~1e-4 of the fp32
+                            definition at H = 4096.                            */
   float logit_scale;     /* s, finite; 1 = off                                    */
   float softcap;         /* c, final_logit_softcapping; <= 0 = off                */
   int64_t ignore_index;  /* usually -100                                          */
@@ -84,6 +86,13 @@ typedef struct flce_problem {
                             argmax are computed for every row).  The valid rows'
                             results and the gradients are the same in both
                             modes up to summation order.                        */
+  int32_t reuse_prepared; /* 0 or 1, read by flce_backward.  1 = reuse the
+                            operands the forward prepared in the same workspace
+                            (fp32 operands rounded to bf16, and with compaction
+                            the scan and the gathered rows) instead of preparing
+                            them again: the workspace must be the one the
+                            forward used, unchanged since, with the same
+                            inputs.  0 = stateless (prepare again).             */
 } flce_problem;
 
 /* Check the problem description only (no HIP call).  0 or FLCE_ERR_*.

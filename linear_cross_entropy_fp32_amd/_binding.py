@@ -37,7 +37,8 @@ class FlceProblem(ctypes.Structure):
                 ("vocab", ctypes.c_int64), ("hidden_dtype", ctypes.c_int32),
                 ("weight_dtype", ctypes.c_int32), ("logit_scale", ctypes.c_float),
                 ("softcap", ctypes.c_float), ("ignore_index", ctypes.c_int64),
-                ("mean_divisor", ctypes.c_float), ("compact_valid", ctypes.c_int32)]
+                ("mean_divisor", ctypes.c_float), ("compact_valid", ctypes.c_int32),
+                ("reuse_prepared", ctypes.c_int32)]
 
 
 class FlceCeProblem(ctypes.Structure):
@@ -93,7 +94,7 @@ def lib() -> ctypes.CDLL:
         L.flce_ce_backward.restype = ctypes.c_int
         L.flce_plan_info.argtypes = [pp, ctypes.POINTER(ctypes.c_int64), ctypes.c_int]
         L.flce_plan_info.restype = ctypes.c_int
-        if L.flce_abi_version() != 1:
+        if L.flce_abi_version() != 2:
             raise RuntimeError("libflce.so ABI version mismatch: rebuild it")
         _lib = L
     return _lib
@@ -107,10 +108,10 @@ def _check(rc: int) -> None:
 def make_problem(n_tokens: int, hidden: int, vocab: int, hidden_dtype: int = FLCE_BF16,
                  weight_dtype: int = FLCE_BF16, logit_scale: float = 1.0, softcap: float = 0.0,
                  ignore_index: int = -100, mean_divisor: float = 0.0,
-                 compact_valid: bool = False) -> FlceProblem:
+                 compact_valid: bool = False, reuse_prepared: bool = False) -> FlceProblem:
     return FlceProblem(n_tokens, hidden, vocab, hidden_dtype, weight_dtype, logit_scale,
                        softcap if softcap else 0.0, ignore_index, mean_divisor,
-                       1 if compact_valid else 0)
+                       1 if compact_valid else 0, 1 if reuse_prepared else 0)
 
 
 def flce_validate(prob: FlceProblem) -> int:
@@ -163,13 +164,14 @@ def _dtype_code(t: torch.Tensor) -> int:
 
 def problem_for(hidden: torch.Tensor, weight: torch.Tensor, logit_scale: float = 1.0,
                 softcap: Optional[float] = None, ignore_index: int = -100,
-                mean_divisor: float = 0.0, compact_valid: bool = False) -> FlceProblem:
+                mean_divisor: float = 0.0, compact_valid: bool = False,
+                reuse_prepared: bool = False) -> FlceProblem:
     if hidden.dim() != 2 or weight.dim() != 2 or hidden.shape[1] != weight.shape[1]:
         raise ValueError(f"hidden {tuple(hidden.shape)} and weight {tuple(weight.shape)} "
                          "must be [N, H] and [V, H]")
     return make_problem(hidden.shape[0], hidden.shape[1], weight.shape[0], _dtype_code(hidden),
                         _dtype_code(weight), float(logit_scale), float(softcap or 0.0),
-                        int(ignore_index), float(mean_divisor), compact_valid)
+                        int(ignore_index), float(mean_divisor), compact_valid, reuse_prepared)
 
 
 def _require(t: torch.Tensor, name: str, device: torch.device) -> None:
@@ -258,9 +260,11 @@ def flce_backward(hidden: torch.Tensor, weight: torch.Tensor, targets: torch.Ten
                   ignore_index: int = -100, mean_divisor: float = 0.0,
                   need_bias_grad: Optional[bool] = None,
                   workspace: Optional[torch.Tensor] = None, out: Optional[dict] = None,
-                  compact_valid: bool = False):
+                  compact_valid: bool = False, reuse_prepared: bool = False):
     """Run ``flce_backward`` on the current stream.  Returns fp32
-    (grad_hidden [N, H], grad_weight [V, H], grad_bias [V] or None)."""
+    (grad_hidden [N, H], grad_weight [V, H], grad_bias [V] or None).
+    reuse_prepared: reuse the operands the forward prepared in ``workspace``
+    (which must then be the forward's, unchanged)."""
     dev = weight.device
     for t, nm in ((hidden, "hidden"), (weight, "weight"), (targets, "targets"), (lse, "lse"),
                   (reduced_i64, "reduced_i64"), (grad_out, "grad_out")):
@@ -272,8 +276,10 @@ def flce_backward(hidden: torch.Tensor, weight: torch.Tensor, targets: torch.Ten
         raise ValueError("per-token grad_out must have N elements")
     if grad_mode != FLCE_GRAD_PER_TOKEN and grad_out.numel() != 1:
         raise ValueError("mean/sum grad_out must have one element")
+    if reuse_prepared and workspace is None:
+        raise ValueError("reuse_prepared needs the forward's workspace")
     prob = problem_for(hidden, weight, logit_scale, softcap, ignore_index, mean_divisor,
-                       compact_valid)
+                       compact_valid, reuse_prepared)
     ws_bytes = flce_workspace_bytes(prob)
     if workspace is None or workspace.numel() < ws_bytes:
         workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)

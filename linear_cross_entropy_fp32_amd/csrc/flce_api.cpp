@@ -83,7 +83,8 @@ struct Plan {
   // row compaction: perm [N] int32, cnt [2] int32, block scratch, compact
   // bf16 hidden rows [N, H] (fp32 hidden: the hi / lo split rows instead)
   size_t off_perm, off_cnt, off_blk, off_hc;
-  size_t off_wsplit;     // fp32 lm_head: its bf16 hi / lo split [2, V, H]
+  size_t off_wsplit;     // fp32 lm_head: rounded to bf16 [V, H]
+  size_t off_zt;         // fp32 operand: the exact target logits [N] (forward part)
   size_t fwd_bytes, bwd_bytes, bytes;
 };
 
@@ -91,6 +92,8 @@ int validate(const flce_problem* p) {
   if (!p) return fail(FLCE_ERR_NULL, "problem is NULL");
   if (p->compact_valid != 0 && p->compact_valid != 1)
     return fail(FLCE_ERR_ARG, "problem.compact_valid must be 0 or 1");
+  if (p->reuse_prepared != 0 && p->reuse_prepared != 1)
+    return fail(FLCE_ERR_ARG, "problem.reuse_prepared must be 0 or 1");
   if (p->n_tokens < 0 || p->n_tokens > kMaxTokens)
     return fail(FLCE_ERR_SHAPE, "n_tokens=%lld out of range [0, 2^23)", (long long)p->n_tokens);
   if (p->vocab < 1 || p->vocab > kMaxRows)
@@ -187,9 +190,9 @@ Plan make_plan(const flce_problem* p) {
 
   size_t off = 0;
   pl.off_wsplit = off;
-  if (p->weight_dtype == FLCE_F32) off += aup(size_t(2) * v * h * 2);
+  if (p->weight_dtype == FLCE_F32) off += aup(size_t(v) * h * 2);
   pl.off_hsplit = off;
-  if (p->hidden_dtype == FLCE_F32) off += aup(size_t(2) * n * h * 2);
+  if (p->hidden_dtype == FLCE_F32) off += aup(size_t(n) * h * 2);
   pl.off_perm = pl.off_cnt = pl.off_blk = pl.off_hc = off;
   if (p->compact_valid && n > 0) {
     pl.off_perm = off;
@@ -202,6 +205,8 @@ Plan make_plan(const flce_problem* p) {
     if (p->hidden_dtype == FLCE_BF16) off += aup(size_t(n) * h * 2);
   }
   const size_t shared_end = off;
+  pl.off_zt = off;
+  if (p->hidden_dtype == FLCE_F32 || p->weight_dtype == FLCE_F32) off += aup(size_t(n) * 4);
   pl.off_part = off;
   off += aup(size_t(pl.n_splits) * n * sizeof(PartState));
   pl.off_bsums = off;
@@ -266,73 +271,71 @@ int hip_check(hipError_t e, const char* what) {
   return FLCE_OK;
 }
 
-// The hidden operand(s) of the kernels, and the row compaction when asked
-// for: perm, the device count of compact rows, and the device count of the
+// The bf16 operands of the products, and the row compaction when asked for:
+// perm, the device count of compact rows, and the device count of the
 // out-of-range targets it leaves out (all null without compaction).
 struct Rows {
-  const uint16_t* w0 = nullptr;   // lm_head (bf16), or the high part of an fp32 one
-  const uint16_t* w1 = nullptr;   // the low part of an fp32 lm_head, else null
-  const uint16_t* h0 = nullptr;
-  const uint16_t* h1 = nullptr;
+  const uint16_t* w0 = nullptr;   // lm_head (bf16), or an fp32 one rounded to bf16
+  const uint16_t* h0 = nullptr;   // hidden (bf16), its compact rows, or fp32 rounded to bf16
   const int* perm = nullptr;
   const int* n_dev = nullptr;
   const int* n_bad = nullptr;
 };
 
+// Prepares the operands in the workspace head: an fp32 lm_head or fp32
+// hidden rounded to bf16, and with compaction the scan and the gathered rows.
+// launch = false only sets the pointers, to what an earlier call on the same
+// workspace and inputs prepared (flce_problem.reuse_prepared).
 int prepare_rows(const flce_problem* p, const Plan& pl, const void* hidden, const void* weight,
-                 const int64_t* targets, char* ws, hipStream_t s, Rows& r) {
+                 const int64_t* targets, char* ws, hipStream_t s, bool launch, Rows& r) {
   const int64_t n = p->n_tokens, h = p->hidden;
   int rc;
   r = Rows{};
   r.w0 = static_cast<const uint16_t*>(weight);
   if (p->weight_dtype == FLCE_F32) {
-    uint16_t* whi = reinterpret_cast<uint16_t*>(ws + pl.off_wsplit);
-    uint16_t* wlo = whi + p->vocab * h;
-    if ((rc = hip_check(launch_split_hidden(static_cast<const float*>(weight), whi, wlo,
-                                            p->vocab * h, s),
-                        "split_weight")))
+    uint16_t* wb = reinterpret_cast<uint16_t*>(ws + pl.off_wsplit);
+    if (launch && (rc = hip_check(launch_round_bf16(static_cast<const float*>(weight), wb,
+                                                    p->vocab * h, s),
+                                  "round_weight")))
       return rc;
-    r.w0 = whi;
-    r.w1 = wlo;
+    r.w0 = wb;
   }
   r.h0 = static_cast<const uint16_t*>(hidden);
   if (n == 0) return FLCE_OK;
-  uint16_t* hi = reinterpret_cast<uint16_t*>(ws + pl.off_hsplit);
-  uint16_t* lo = hi + n * h;
+  uint16_t* hb = reinterpret_cast<uint16_t*>(ws + pl.off_hsplit);
   if (p->compact_valid) {
     int* perm = reinterpret_cast<int*>(ws + pl.off_perm);
     int* cnt = reinterpret_cast<int*>(ws + pl.off_cnt);
     int* blk = reinterpret_cast<int*>(ws + pl.off_blk);
-    if ((rc = hip_check(launch_compact(targets, (int)n, p->ignore_index, (int)p->vocab, blk, cnt,
-                                       perm, s),
-                        "compact")))
+    if (launch && (rc = hip_check(launch_compact(targets, (int)n, p->ignore_index, (int)p->vocab,
+                                                 blk, cnt, perm, s),
+                                  "compact")))
       return rc;
     r.perm = perm;
     r.n_dev = cnt;
     r.n_bad = cnt + 1;
     if (p->hidden_dtype == FLCE_F32) {
-      if ((rc = hip_check(launch_gather_split(static_cast<const float*>(hidden), perm, cnt, n, h,
-                                              hi, lo, s),
-                          "gather_split")))
+      if (launch && (rc = hip_check(launch_gather_round(static_cast<const float*>(hidden), perm,
+                                                        cnt, n, h, hb, s),
+                                    "gather_round")))
         return rc;
-      r.h0 = hi;
-      r.h1 = lo;
+      r.h0 = hb;
     } else {
       uint16_t* hc = reinterpret_cast<uint16_t*>(ws + pl.off_hc);
-      if ((rc = hip_check(launch_gather_rows(static_cast<const uint16_t*>(hidden), perm, cnt, n,
-                                             h, hc, s),
-                          "gather_rows")))
+      if (launch && (rc = hip_check(launch_gather_rows(static_cast<const uint16_t*>(hidden), perm,
+                                                       cnt, n, h, hc, s),
+                                    "gather_rows")))
         return rc;
       r.h0 = hc;
     }
     return FLCE_OK;
   }
   if (p->hidden_dtype == FLCE_F32) {
-    if ((rc = hip_check(launch_split_hidden(static_cast<const float*>(hidden), hi, lo, n * h, s),
-                        "split_hidden")))
+    if (launch && (rc = hip_check(launch_round_bf16(static_cast<const float*>(hidden), hb, n * h,
+                                                    s),
+                                  "round_hidden")))
       return rc;
-    r.h0 = hi;
-    r.h1 = lo;
+    r.h0 = hb;
   }
   return FLCE_OK;
 }
@@ -379,7 +382,7 @@ using namespace flce;
 
 extern "C" {
 
-int flce_abi_version(void) { return 1; }
+int flce_abi_version(void) { return 2; }
 
 int flce_set_timing_events(int kernel, void* const* events, int n_pairs) {
   g_err[0] = 0;
@@ -531,14 +534,33 @@ int flce_forward(const flce_problem* p, const void* hidden, const void* weight,
   char* ws = static_cast<char*>(workspace);
 
   Rows rows;
-  if ((rc = prepare_rows(p, pl, hidden, weight, targets, ws, s, rows))) return rc;
+  if ((rc = prepare_rows(p, pl, hidden, weight, targets, ws, s, true, rows))) return rc;
   PartState* part = reinterpret_cast<PartState*>(ws + pl.off_part);
+  // with an fp32 operand rounded for the products, the target logit comes from
+  // the unrounded operands
+  float* zt_exact = nullptr;
+  if (n > 0 && (p->hidden_dtype == FLCE_F32 || p->weight_dtype == FLCE_F32)) {
+    zt_exact = reinterpret_cast<float*>(ws + pl.off_zt);
+    TargetArgs ta{};
+    ta.hidden = hidden;
+    ta.weight = weight;
+    ta.bias = bias;
+    ta.tgt = targets;
+    ta.h_f32 = p->hidden_dtype == FLCE_F32;
+    ta.w_f32 = p->weight_dtype == FLCE_F32;
+    ta.n = n;
+    ta.hdim = p->hidden;
+    ta.v = p->vocab;
+    ta.ignore_index = p->ignore_index;
+    ta.scale = p->logit_scale;
+    ta.softcap = p->softcap;
+    ta.zt = zt_exact;
+    if ((rc = hip_check(launch_target_logits(ta, s), "target_logits"))) return rc;
+  }
   if (n > 0) {
     FwdArgs a{};
     a.w = rows.w0;
-    a.w1 = rows.w1;
     a.h0 = rows.h0;
-    a.h1 = rows.h1;
     a.bias = bias;
     a.tgt = targets;
     a.perm = rows.perm;
@@ -575,6 +597,7 @@ int flce_forward(const flce_problem* p, const void* hidden, const void* weight,
   f.hit = hit;
   f.argmax = argmax;
   f.block_sums = reinterpret_cast<BlockSums*>(ws + pl.off_bsums);
+  f.zt_exact = zt_exact;
   f.perm = rows.perm;
   f.n_dev = rows.n_dev;
   return hip_check(launch_fwd_finalize(f, pl.fin_blocks, p->mean_divisor > 0 ? p->mean_divisor : 0.f,
@@ -640,18 +663,16 @@ int flce_backward(const flce_problem* p, const void* hidden, const void* weight,
   }
 
   Rows rows;
-  if ((rc = prepare_rows(p, pl, hidden, weight, targets, ws, s, rows))) return rc;
+  if ((rc = prepare_rows(p, pl, hidden, weight, targets, ws, s, p->reuse_prepared == 0, rows)))
+    return rc;
   const uint16_t* h0 = rows.h0;
-  const uint16_t* h1 = rows.h1;
   const bool slots = pl.gh_splits > 1 || rows.perm != nullptr;   // grad_hidden via the slots
   uint16_t* dz = reinterpret_cast<uint16_t*>(ws + pl.off_dz);
   float* ghpart = reinterpret_cast<float*>(ws + pl.off_ghpart);
 
   DzArgs d{};
   d.w = rows.w0;
-  d.w1 = rows.w1;
   d.h0 = h0;
-  d.h1 = h1;
   d.bias = bias;
   d.tgt = targets;
   d.lse = lse;
@@ -697,7 +718,7 @@ int flce_backward(const flce_problem* p, const void* hidden, const void* weight,
                         "bwd_dz")))
       return rc;
 
-    g.w = rows.w0 + c0 * h;   // an fp32 lm_head enters grad_hidden as its high part
+    g.w = rows.w0 + c0 * h;   // an fp32 lm_head enters grad_hidden rounded to bf16
     g.width = (int)width;
     g.gh_accumulate = c > 0;
     g.gw = grad_weight + c0 * h;

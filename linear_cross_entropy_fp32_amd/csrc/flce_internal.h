@@ -30,10 +30,8 @@ struct BlockSums {
 };
 
 struct FwdArgs {
-  const uint16_t* w;     // [V, H] bf16 (lm_head, or its high part)
-  const uint16_t* w1;    // [V, H] bf16 low part of an fp32 lm_head, or null
-  const uint16_t* h0;    // [N, H] bf16 (hidden, or its high part)
-  const uint16_t* h1;    // [N, H] bf16 low part of an fp32 hidden, or null
+  const uint16_t* w;     // [V, H] bf16 (lm_head, or an fp32 one rounded to bf16)
+  const uint16_t* h0;    // [N, H] bf16 (hidden, or fp32 hidden rounded to bf16)
   const float* bias;     // [V] or null
   const int64_t* tgt;    // [N]
   int n, hdim, v;
@@ -59,6 +57,10 @@ struct FinalArgs {
   uint8_t* hit;
   int32_t* argmax;       // may be null
   BlockSums* block_sums;
+  // the target logits in base-2 units [N] (by original row), computed from the
+  // unrounded operands when an fp32 operand was rounded for the products; or
+  // null, and the target value of the tile fold is used
+  const float* zt_exact;
   // row compaction (both null without it): compact row c is row perm[c]; rows
   // c >= *n_dev get zero outputs (lse 0, argmax -1)
   const int* perm;
@@ -66,10 +68,8 @@ struct FinalArgs {
 };
 
 struct DzArgs {
-  const uint16_t* w;     // [V, H] bf16 (lm_head, or its high part)
-  const uint16_t* w1;    // [V, H] bf16 low part of an fp32 lm_head, or null
-  const uint16_t* h0;
-  const uint16_t* h1;
+  const uint16_t* w;     // [V, H] bf16 (lm_head, or an fp32 one rounded to bf16)
+  const uint16_t* h0;    // [N, H] bf16 (hidden, or fp32 hidden rounded to bf16)
   const float* bias;
   const int64_t* tgt;
   const float* lse;      // [N], natural log units
@@ -101,7 +101,7 @@ struct ContractArgs {
   const uint16_t* dz;    // [N, ldz] bf16
   int64_t ldz;
   const uint16_t* w;     // lm_head rows of the chunk: w + c0 * H
-  const uint16_t* h;     // [N, H] bf16 (the high part for fp32 hidden)
+  const uint16_t* h;     // [N, H] bf16 (fp32 hidden rounded to bf16)
   int n, hdim, width;    // tokens, hidden, vocab rows in the chunk
   int gh_splits, gh_kps, gh_m_tiles, n_tiles;
   int gw_m_tiles, gw_rows_per_unit;   // unit u: gh split u, then gw tile rows of the unit
@@ -111,10 +111,24 @@ struct ContractArgs {
   const int* n_dev;      // row compaction: only dz rows c < *n_dev are used; else null
 };
 
-// hi = bf16(h), lo = bf16(h - hi) for count values (a multiple of 8; the
-// pointers 16-byte aligned): fp32 hidden states or an fp32 lm_head.
-hipError_t launch_split_hidden(const float* h, uint16_t* hi, uint16_t* lo, int64_t count,
-                               hipStream_t s);
+// out = bf16(x) (round to nearest even) for count values (a multiple of 8;
+// the pointers 16-byte aligned): fp32 hidden states or an fp32 lm_head.
+hipError_t launch_round_bf16(const float* x, uint16_t* out, int64_t count, hipStream_t s);
+// The exact target logit of every valid row, in base-2 units (see final_u):
+// the dot product of the unrounded hidden row (bf16 or fp32) and the
+// unrounded lm_head row of the target (bf16 or fp32), accumulated in double,
+// then + bias, * scale, softcap.  One wave per row; rows without a loss get 0.
+struct TargetArgs {
+  const void* hidden;    // [N, H]
+  const void* weight;    // [V, H]
+  const float* bias;     // [V] or null
+  const int64_t* tgt;    // [N]
+  int h_f32, w_f32;
+  int64_t n, hdim, v, ignore_index;
+  double scale, softcap; // logit_scale; c (<= 0: none)
+  float* zt;             // [N] out
+};
+hipError_t launch_target_logits(const TargetArgs& a, hipStream_t s);
 hipError_t launch_fwd_stats(const FwdArgs& a, bool cap, bool fixed_ref, hipStream_t s);
 // n_bad_extra: null, or a device count of out-of-range targets that the
 // finalize did not see (rows left out by the row compaction)
@@ -134,13 +148,13 @@ hipError_t launch_colsum(const uint16_t* dz, int64_t ldz, int n_tok, int width, 
 // Row compaction (see compact_scatter_kernel): perm [N], cnt [2] = {rows that
 // carry a loss, out-of-range targets}; blk: 2 * cdiv(N, 256) ints of scratch.
 // Then the hidden rows of the first cnt[0] compact rows are gathered into
-// out_h (bf16 hidden), or split into out_hi / out_lo (fp32 hidden).
+// out (bf16 hidden), or gathered and rounded to bf16 (fp32 hidden).
 hipError_t launch_compact(const int64_t* tgt, int n, int64_t ignore, int v, int* blk, int* cnt,
                           int* perm, hipStream_t s);
 hipError_t launch_gather_rows(const uint16_t* h, const int* perm, const int* cnt, int64_t n,
                               int64_t hdim, uint16_t* out, hipStream_t s);
-hipError_t launch_gather_split(const float* h, const int* perm, const int* cnt, int64_t n,
-                               int64_t hdim, uint16_t* hi, uint16_t* lo, hipStream_t s);
+hipError_t launch_gather_round(const float* h, const int* perm, const int* cnt, int64_t n,
+                               int64_t hdim, uint16_t* out, hipStream_t s);
 hipError_t launch_fill_zero(float* p, int64_t count, hipStream_t s);
 
 }  // namespace flce

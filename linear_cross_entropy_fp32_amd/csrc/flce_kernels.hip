@@ -134,30 +134,62 @@ __device__ __forceinline__ const float* bias_block(const float* rows, int t) {
   return rows + (t % kRowDmaBufs) * 256 + (threadIdx.x >> 6) * 64;
 }
 
-// --------------------------------------------------- fp32 hidden: hi / lo split
-// h = hi + lo with hi = bf16(h), lo = bf16(h - hi); the lm_head is exact in
-// bf16, so two bf16 MFMA passes reproduce the fp32 product to ~2^-17.
-// Eight values per thread (count is a multiple of 8: rows of H values, H % 8
-// == 0), read and written 16 bytes at a time.
-__global__ void split_hidden_kernel(const float* __restrict__ h, uint16_t* __restrict__ hi,
-                                    uint16_t* __restrict__ lo, int64_t count) {
+// ------------------------------------------- fp32 operands: rounded to bf16
+// An fp32 hidden state or lm_head enters the MFMA products rounded to bf16
+// (round to nearest even).  The logits then carry the operands' rounding
+// (~1e-3 at H = 4096), which averages out in lse, entropy and the softmax,
+// while the target logit, which the loss takes directly, is computed exactly
+// from the unrounded operands (target_logit_kernel).  Eight values per
+// thread (count is a multiple of 8), read and written 16 bytes at a time.
+__global__ void round_bf16_kernel(const float* __restrict__ x, uint16_t* __restrict__ out,
+                                  int64_t count) {
   const int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 8;
   if (i >= count) return;
   typedef float f32x4 __attribute__((ext_vector_type(4)));
-  const f32x4 x0 = *reinterpret_cast<const f32x4*>(h + i);
-  const f32x4 x1 = *reinterpret_cast<const f32x4*>(h + i + 4);
-  const float v[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
-  u32x4 ph, pl;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const float a = v[2 * k], b = v[2 * k + 1];
-    ph[k] = pack_bf16x2(a, b);
-    const float ah = __builtin_bit_cast(float, ph[k] << 16);
-    const float bh = __builtin_bit_cast(float, ph[k] & 0xffff0000u);
-    pl[k] = pack_bf16x2(a - ah, b - bh);
+  const f32x4 x0 = *reinterpret_cast<const f32x4*>(x + i);
+  const f32x4 x1 = *reinterpret_cast<const f32x4*>(x + i + 4);
+  u32x4 o;
+  o[0] = pack_bf16x2(x0[0], x0[1]);
+  o[1] = pack_bf16x2(x0[2], x0[3]);
+  o[2] = pack_bf16x2(x1[0], x1[1]);
+  o[3] = pack_bf16x2(x1[2], x1[3]);
+  *reinterpret_cast<u32x4*>(out + i) = o;
+}
+
+// The target logit of row n from the unrounded operands: one wave per row,
+// lanes striding over H, products and sums in double, then a fixed xor tree;
+// + bias, * scale, softcap in double, returned in base-2 units.
+constexpr int kTargetRowsPerBlock = 4;
+__global__ void __launch_bounds__(64 * kTargetRowsPerBlock)
+target_logit_kernel(const TargetArgs a) {
+  const int64_t n = (int64_t)blockIdx.x * kTargetRowsPerBlock + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (n >= a.n) return;
+  const int64_t t = a.tgt[n];
+  if (t == a.ignore_index || t < 0 || t >= a.v) {
+    if (lane == 0) a.zt[n] = 0.f;
+    return;
   }
-  *reinterpret_cast<u32x4*>(hi + i) = ph;
-  *reinterpret_cast<u32x4*>(lo + i) = pl;
+  double acc = 0.0;
+  for (int64_t k = lane; k < a.hdim; k += 64) {
+    const int64_t hi = n * a.hdim + k, wi = t * a.hdim + k;
+    const double hv = a.h_f32 ? (double)static_cast<const float*>(a.hidden)[hi]
+                              : (double)__builtin_bit_cast(
+                                    float, (uint32_t)static_cast<const uint16_t*>(a.hidden)[hi]
+                                               << 16);
+    const double wv = a.w_f32 ? (double)static_cast<const float*>(a.weight)[wi]
+                              : (double)__builtin_bit_cast(
+                                    float, (uint32_t)static_cast<const uint16_t*>(a.weight)[wi]
+                                               << 16);
+    acc = fma(hv, wv, acc);
+  }
+  for (int m = 32; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
+  if (lane != 0) return;
+  double z = acc;
+  if (a.bias) z += (double)a.bias[t];
+  z *= a.scale;
+  if (a.softcap > 0.0) z = a.softcap * tanh(z / a.softcap);
+  a.zt[n] = (float)(z * 1.4426950408889634);
 }
 
 // ------------------------------------------------------------ row compaction
@@ -283,37 +315,19 @@ __global__ void gather_rows_kernel(const uint16_t* __restrict__ h, const int* __
       *reinterpret_cast<const u32x4*>(h + (int64_t)perm[c] * hdim + k);
 }
 
-// fp32 hidden: gather and split in one pass, hi = bf16(h), lo = bf16(h - hi).
-__global__ void gather_split_kernel(const float* __restrict__ h, const int* __restrict__ perm,
+// fp32 hidden: gather and round to bf16 in one pass.
+__global__ void gather_round_kernel(const float* __restrict__ h, const int* __restrict__ perm,
                                     const int* __restrict__ cnt, int64_t hdim,
-                                    uint16_t* __restrict__ hi, uint16_t* __restrict__ lo,
-                                    int64_t n) {
+                                    uint16_t* __restrict__ out, int64_t n) {
   const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t per_row = hdim / 8;
   const int64_t c = t / per_row, k = (t % per_row) * 8;
   if (c >= n || c >= cnt[0]) return;
   const float* src = h + (int64_t)perm[c] * hdim + k;
-  u32x4 ph, pl;
+  u32x4 o;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float a = src[2 * i], b = src[2 * i + 1];
-    ph[i] = pack_bf16x2(a, b);
-    const float ah = __builtin_bit_cast(float, ph[i] << 16);
-    const float bh = __builtin_bit_cast(float, ph[i] & 0xffff0000u);
-    pl[i] = pack_bf16x2(a - ah, b - bh);
-  }
-  *reinterpret_cast<u32x4*>(hi + c * hdim + k) = ph;
-  *reinterpret_cast<u32x4*>(lo + c * hdim + k) = pl;
-}
-
-// The K-loop segments of a logit tile: W . h, plus W . h_lo for fp32 hidden
-// and W_lo . h for an fp32 lm_head (h_lo . W_lo, below 2^-16 of the product,
-// is left out).
-__device__ __forceinline__ SegPlan logit_segments(bool h_split, bool w_split) {
-  if (h_split && w_split) return SegPlan{3, 0b100, 0b010};
-  if (h_split) return SegPlan{2, 0, 0b10};
-  if (w_split) return SegPlan{2, 0b10, 0};
-  return SegPlan{1, 0, 0};
+  for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(src[2 * i], src[2 * i + 1]);
+  *reinterpret_cast<u32x4*>(out + c * hdim + k) = o;
 }
 
 // ------------------------------------------------------------- forward: K1
@@ -429,7 +443,7 @@ struct FwdEpilogue {
 // into the per-token states held in registers.  At the end of the split the
 // states of the two half-waves and of the two waves sharing a token are merged
 // and written as one partial state per (split, token).
-template <bool CAP, bool FIXED, bool BIAS, bool WSPLIT>
+template <bool CAP, bool FIXED, bool BIAS>
 __global__ void __launch_bounds__(kThreads, kLogitWgsPerCu)
 fwd_stats_kernel(const FwdArgs a) {
   __shared__ __attribute__((aligned(16))) char lds[LogitTile::kLdsBytes];
@@ -455,10 +469,8 @@ fwd_stats_kernel(const FwdArgs a) {
   }
   const int vt_begin = sp * a.tiles_per_split;
   const int ntiles = min(a.n_voc_tiles, vt_begin + a.tiles_per_split) - vt_begin;
-  const Operand opA0{a.w, a.hdim, vt_begin * kLogitTileV, a.v, a.hdim};
-  const Operand opA1{a.w1 ? a.w1 : a.w, a.hdim, vt_begin * kLogitTileV, a.v, a.hdim};
-  const Operand opB0{a.h0, a.hdim, n0, n_rows, a.hdim};
-  const Operand opB1{a.h1 ? a.h1 : a.h0, a.hdim, n0, n_rows, a.hdim};
+  const Operand opA{a.w, a.hdim, vt_begin * kLogitTileV, a.v, a.hdim};
+  const Operand opB{a.h0, a.hdim, n0, n_rows, a.hdim};
   __shared__ __attribute__((aligned(16))) float rows[BIAS ? kRowDmaBytes / 4 : 4];
   RowDma rd{};
   if constexpr (BIAS)
@@ -466,8 +478,7 @@ fwd_stats_kernel(const FwdArgs a) {
                 vt_begin * kLogitTileV};
   FwdEpilogue<CAP, FIXED, BIAS> epi{a, st, tgt, rows, vt_begin, wm, half};
   LogitTile T;
-  T.run_stream<WSPLIT, BIAS>(lds, opA0, opA1, opB0, opB1,
-                             logit_segments(a.h1 != nullptr, WSPLIT), a.hdim, ntiles, epi, rd);
+  T.run_stream<BIAS>(lds, opA, opB, a.hdim, ntiles, epi, rd);
 
 #pragma unroll
   for (int j = 0; j < kColumns; ++j) {
@@ -544,7 +555,8 @@ fwd_finalize_kernel(const FinalArgs a) {
     float loss = 0.f, ent = 0.f;
     uint8_t hit = 0;
     if (valid) {
-      loss = (lse2 - st.zt) * kLn2;
+      const float zt = a.zt_exact ? a.zt_exact[row] : st.zt;
+      loss = (lse2 - zt) * kLn2;
       ent = (lse2 - st.t / st.s) * kLn2;
       hit = (st.bi == (int)t) ? 1 : 0;
     }
@@ -763,7 +775,7 @@ struct DzEpilogue {
   }
 };
 
-template <bool CAP, bool BIAS, bool WSPLIT>
+template <bool CAP, bool BIAS>
 __global__ void __launch_bounds__(kThreads, kLogitWgsPerCu)
 bwd_dz_kernel(const DzArgs a) {
   __shared__ __attribute__((aligned(16))) char lds[LogitTile::kLdsBytes];
@@ -793,10 +805,8 @@ bwd_dz_kernel(const DzArgs a) {
   }
   const int vt_begin = grp * a.tiles_per_wg;
   const int ntiles = min(a.chunk_tiles, vt_begin + a.tiles_per_wg) - vt_begin;
-  const Operand opA0{a.w, a.hdim, a.c0 + vt_begin * kLogitTileV, a.v, a.hdim};
-  const Operand opA1{a.w1 ? a.w1 : a.w, a.hdim, a.c0 + vt_begin * kLogitTileV, a.v, a.hdim};
-  const Operand opB0{a.h0, a.hdim, n0, n_rows, a.hdim};
-  const Operand opB1{a.h1 ? a.h1 : a.h0, a.hdim, n0, n_rows, a.hdim};
+  const Operand opA{a.w, a.hdim, a.c0 + vt_begin * kLogitTileV, a.v, a.hdim};
+  const Operand opB{a.h0, a.hdim, n0, n_rows, a.hdim};
   __shared__ __attribute__((aligned(16))) float rows[BIAS ? kRowDmaBytes / 4 : 4];
   RowDma rd{};
   if constexpr (BIAS)
@@ -805,8 +815,7 @@ bwd_dz_kernel(const DzArgs a) {
   DzEpilogue<CAP, BIAS> epi{a, gs, nl, tgt, rows, vt_begin, wm, half,
                            __builtin_amdgcn_readfirstlane(n0 + wn * (kLogitTileN / 2))};
   LogitTile T;
-  T.run_stream<WSPLIT, BIAS>(lds, opA0, opA1, opB0, opB1,
-                             logit_segments(a.h1 != nullptr, WSPLIT), a.hdim, ntiles, epi, rd);
+  T.run_stream<BIAS>(lds, opA, opB, a.hdim, ntiles, epi, rd);
 }
 
 // ------------------------------------------- contractions over a dz chunk
@@ -987,11 +996,16 @@ static inline unsigned grid1(int64_t count, int block) {
   return (unsigned)((count + block - 1) / block);
 }
 
-hipError_t launch_split_hidden(const float* h, uint16_t* hi, uint16_t* lo, int64_t count,
-                               hipStream_t s) {
+hipError_t launch_round_bf16(const float* x, uint16_t* out, int64_t count, hipStream_t s) {
   if (count == 0) return hipSuccess;
   if (count % 8 != 0) return hipErrorInvalidValue;   // whole rows of H % 8 == 0 values
-  split_hidden_kernel<<<grid1(count / 8, 256), 256, 0, s>>>(h, hi, lo, count);
+  round_bf16_kernel<<<grid1(count / 8, 256), 256, 0, s>>>(x, out, count);
+  return hipGetLastError();
+}
+
+hipError_t launch_target_logits(const TargetArgs& a, hipStream_t s) {
+  if (a.n == 0) return hipSuccess;
+  target_logit_kernel<<<grid1(a.n, kTargetRowsPerBlock), 64 * kTargetRowsPerBlock, 0, s>>>(a);
   return hipGetLastError();
 }
 
@@ -999,11 +1013,7 @@ hipError_t launch_fwd_stats(const FwdArgs& a, bool cap, bool fixed_ref, hipStrea
   const unsigned grid = (unsigned)(a.n_tok_tiles * a.n_splits);
   if (grid == 0) return hipSuccess;
   const bool bias = a.bias != nullptr;
-#define FLCE_FWD(C, F, B)                                               \
-  do {                                                                  \
-    if (a.w1) fwd_stats_kernel<C, F, B, true><<<grid, kThreads, 0, s>>>(a); \
-    else fwd_stats_kernel<C, F, B, false><<<grid, kThreads, 0, s>>>(a);     \
-  } while (0)
+#define FLCE_FWD(C, F, B) fwd_stats_kernel<C, F, B><<<grid, kThreads, 0, s>>>(a)
   if (cap && fixed_ref) {
     if (bias) FLCE_FWD(true, true, true); else FLCE_FWD(true, true, false);
   } else if (cap) {
@@ -1029,11 +1039,7 @@ hipError_t launch_bwd_dz(const DzArgs& a, bool cap, hipStream_t s) {
   const unsigned grid = (unsigned)(a.n_tok_tiles * groups);
   if (grid == 0) return hipSuccess;
   const bool bias = a.bias != nullptr;
-#define FLCE_DZ(C, B)                                                \
-  do {                                                               \
-    if (a.w1) bwd_dz_kernel<C, B, true><<<grid, kThreads, 0, s>>>(a); \
-    else bwd_dz_kernel<C, B, false><<<grid, kThreads, 0, s>>>(a);     \
-  } while (0)
+#define FLCE_DZ(C, B) bwd_dz_kernel<C, B><<<grid, kThreads, 0, s>>>(a)
   if (cap) {
     if (bias) FLCE_DZ(true, true); else FLCE_DZ(true, false);
   } else {
@@ -1090,11 +1096,11 @@ hipError_t launch_gather_rows(const uint16_t* h, const int* perm, const int* cnt
   return hipGetLastError();
 }
 
-hipError_t launch_gather_split(const float* h, const int* perm, const int* cnt, int64_t n,
-                               int64_t hdim, uint16_t* hi, uint16_t* lo, hipStream_t s) {
+hipError_t launch_gather_round(const float* h, const int* perm, const int* cnt, int64_t n,
+                               int64_t hdim, uint16_t* out, hipStream_t s) {
   const int64_t threads = n * (hdim / 8);
   if (threads == 0) return hipSuccess;
-  gather_split_kernel<<<grid1(threads, 256), 256, 0, s>>>(h, perm, cnt, hdim, hi, lo, n);
+  gather_round_kernel<<<grid1(threads, 256), 256, 0, s>>>(h, perm, cnt, hdim, out, n);
   return hipGetLastError();
 }
 

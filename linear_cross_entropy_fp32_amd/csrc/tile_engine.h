@@ -81,12 +81,6 @@ struct Operand {
   int k_bound;
 };
 
-// Segments of a streamed K loop (see Tile::run_stream): n in 1..3; bit s of a
-// (b) selects the second A (B) operand for segment s.
-struct SegPlan {
-  int n, a, b;
-};
-
 constexpr uint32_t kOutOfRange = 0x80000000u;   // buffer offset that reads as zero
 
 // Buffer descriptor whose base is the tile's first element; loads past
@@ -485,38 +479,28 @@ struct Tile {
   }
 
   // Streams `ntiles` tiles that share the B operand and take A rows
-  // a.row0 + t * BM (t = 0 .. ntiles-1), with the prefetch running across tile
-  // boundaries.  Each tile sums sg.n segments of the K range [0, k_end): segment
-  // s multiplies A operand (sg.a >> s) & 1 (a0 / a1) by B operand (sg.b >> s)
-  // & 1 (b0 / b1), which is how split fp32 operands (bf16 high + low parts)
-  // enter.  After the last slice of tile t, epi(t, *this, free) consumes acc
-  // (the next tile starts from zero again); `free` is an LDS stage (kStage
-  // bytes) that no wave reads or loads into until the epilogue returns, when
-  // Epi::kUsesLds asks for it (one extra barrier per tile), else null.  A2:
-  // whether the second A operand is used at all (compile time; without it
-  // sg.a must be 0 and a1_op is ignored, and the loop is the one-A loop).
-  template <bool A2, bool ROWS, class Epi>
-  __device__ __forceinline__ void run_stream(char* lds, const Operand a0_op, const Operand a1_op,
-                                             const Operand b0_op, const Operand b1_op,
-                                             const SegPlan sg, int k_end, int ntiles, Epi& epi,
+  // a.row0 + t * BM (t = 0 .. ntiles-1), each summed over the K range
+  // [0, k_end), with the prefetch running across tile boundaries.  After the
+  // last slice of tile t, epi(t, *this, free) consumes acc (the next tile
+  // starts from zero again); `free` is an LDS stage (kStage bytes) that no
+  // wave reads or loads into until the epilogue returns, when Epi::kUsesLds
+  // asks for it (one extra barrier per tile), else null.  ROWS: per-row values
+  // of the A rows arrive by LDS DMA with each tile's first slice (see RowDma).
+  template <bool ROWS, class Epi>
+  __device__ __forceinline__ void run_stream(char* lds, const Operand a_op, const Operand b_op,
+                                             int k_end, int ntiles, Epi& epi,
                                              const RowDma& rd = RowDma{}) {
     static_assert(!ROWS || BM == 128, "row values: 64 rows per wave");
-    const int kt_seg = (k_end + kBK - 1) / kBK;
-    const int kt_tile = kt_seg * sg.n;
+    const int kt_tile = (k_end + kBK - 1) / kBK;
     if (kt_tile <= 0 || ntiles <= 0) return;
-    const typename SB::Src b0 = SB::source(b0_op);
-    const typename SB::Src b1 = SB::source(sg.b ? b1_op : b0_op);
-    const int past = sg.n * kt_seg;   // a slice index that reads zero in every segment
-    // issue pointer: tile it, slice is, its A sources and ring stage
+    const typename SB::Src b = SB::source(b_op);
+    const int past = kt_tile;   // a slice index that reads zero
+    // issue pointer: tile it, slice is, its A source, ring stage and row buffer
     int it = 0, is = 0, islot = 0, ibuf = 0;
-    Operand ao0 = a0_op, ao1 = a1_op;
-    typename SA::Src a0 = SA::source(ao0);
-    typename SA::Src a1 = a0;
-    if constexpr (A2) a1 = SA::source(ao1);
+    Operand ao = a_op;
+    typename SA::Src a = SA::source(ao);
     auto issue_next = [&]() {
-      const int kt = it < ntiles ? is : past;
-      const int seg = (kt >= kt_seg ? 1 : 0) + (sg.n > 2 && kt >= 2 * kt_seg ? 1 : 0);
-      const int k0 = (kt - seg * kt_seg) * kBK;
+      const int k0 = (it < ntiles ? is : past) * kBK;
       char* buf = lds + islot * kStage;
       if constexpr (ROWS) {
         if (is == 0 && it < ntiles) {
@@ -526,21 +510,14 @@ struct Tile {
           ibuf = ibuf == kRowDmaBufs - 1 ? 0 : ibuf + 1;
         }
       }
-      if constexpr (A2)
-        SA::issue(((sg.a >> seg) & 1) ? a1 : a0, buf, k0);
-      else
-        SA::issue(a0, buf, k0);
-      SB::issue(((sg.b >> seg) & 1) ? b1 : b0, buf + kLdsA, k0);
+      SA::issue(a, buf, k0);
+      SB::issue(b, buf + kLdsA, k0);
       islot = islot == kStages - 1 ? 0 : islot + 1;
       if (++is == kt_tile) {
         is = 0;
         if (++it < ntiles) {
-          ao0.row0 += BM;
-          a0 = SA::source(ao0);
-          if constexpr (A2) {
-            ao1.row0 += BM;
-            a1 = SA::source(ao1);
-          }
+          ao.row0 += BM;
+          a = SA::source(ao);
         }
       }
     };

@@ -359,3 +359,35 @@ def test_argmax_targets_zipf_shape_class():
     assert np.all(g["hit"].numpy()[sure] == 1)
     assert np.array_equal(g["argmax"].numpy()[sure], am[sure])
     assert sure.sum() >= 100
+
+
+@pytest.mark.parametrize("hd,wd,compact", [("f32", "bf16", False), ("bf16", "f32", False),
+                                           ("f32", "f32", True), ("bf16", "bf16", True)])
+def test_backward_reuses_prepared_operands(hd, wd, compact):
+    """flce_problem.reuse_prepared: the backward reads the bf16-rounded fp32
+    operands (and with compaction the scan and gathered rows) that the
+    forward left in the same workspace; the gradients are bitwise those of a
+    backward that prepares them again."""
+    w = synth.small_workload(700, 136, 3000, 51, hidden_dtype=hd, weight_dtype=wd, softcap=30.0,
+                             bias=True, prompt_frac=0.5 if compact else 0.0, prompt_block=128,
+                             reduction="none")
+    inp = synth.make_inputs(w)
+    dev = "cuda:0"
+    h, wt, b, t = (inp.hidden.to(dev), inp.weight.to(dev), inp.bias.to(dev),
+                   inp.targets.to(dev))
+    go = inp.grad_out.to(dev)
+    prob = flce._binding.problem_for(h, wt, w.logit_scale, w.softcap, compact_valid=compact)
+    ws = torch.empty(flce.flce_workspace_bytes(prob), dtype=torch.uint8, device=dev)
+    say(f"[parity] reuse_prepared {hd}/{wd} compact={compact}")
+    f = flce.flce_forward(h, wt, t, b, w.logit_scale, w.softcap, workspace=ws,
+                          compact_valid=compact)
+    reused = flce.flce_backward(h, wt, t, f["lse"], f["reduced_i64"], flce.FLCE_GRAD_PER_TOKEN,
+                                go, b, w.logit_scale, w.softcap, workspace=ws,
+                                compact_valid=compact, reuse_prepared=True)
+    fresh = flce.flce_backward(h, wt, t, f["lse"], f["reduced_i64"], flce.FLCE_GRAD_PER_TOKEN,
+                               go, b, w.logit_scale, w.softcap, compact_valid=compact)
+    torch.cuda.synchronize()
+    for a, c in zip(reused, fresh):
+        assert torch.equal(a, c)
+    o, og = _oracle_all(w, inp)
+    check_grad(reused[1].cpu().numpy(), og["grad_weight"], "grad_weight", w.name)
