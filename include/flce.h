@@ -246,19 +246,28 @@ int flce_ce_backward(const flce_ce_problem* p, void* grad_logits, const int64_t*
  * call).  Writes min(n_out, FLCE_PLAN_FIELDS) values to out (host memory), in
  * this order, and returns that count, or a negative FLCE_ERR_* code for an
  * invalid problem or a null out:
- *   0 chunk_rows       vocabulary rows per backward chunk (Vc, a multiple of 128)
+ *   0 chunk_rows       vocabulary rows per backward chunk (Vc, a multiple of
+ *                      dz_tile_rows)
  *   1 n_chunks         backward chunks (contraction launches per backward)
  *   2 fwd_splits       vocabulary splits of the forward statistics
- *   3 fwd_tiles_per_split  128-row vocabulary tiles per forward split
- *   4 dz_tiles_per_wg  vocabulary tiles per workgroup of the dz recompute
+ *   3 fwd_tiles_per_split  vocabulary tiles (fwd_tile_rows each) per forward split
+ *   4 dz_tiles_per_wg  vocabulary tiles (dz_tile_rows each) per workgroup of
+ *                      the dz recompute
  *   5 gh_splits        grad_hidden split-K slots per chunk
  *   6 gh_rows_per_split  vocabulary rows per slot (a multiple of 32)
- *   7 window_token_tiles  token tiles per 64-workgroup window of the logit order
+ *   7 window_token_tiles  token tiles per window of the logit order (a window
+ *                      is what one XCD holds at once: 64 workgroups of the
+ *                      128-row tile, 32 of the 256-row one)
  *   8 token_tile_fastest  1: windows take the token tile fastest
  *   9 fwd_workspace_bytes, 10 bwd_workspace_bytes, 11 workspace_bytes
  *  12 dz_chunk_bytes   N * chunk_rows * 2 (the largest (tokens x vocab) buffer)
+ *  13 fwd_tile_rows    vocabulary rows per logit tile of the forward (128, or
+ *                      256 from H = 1024 on)
+ *  14 dz_tile_rows     vocabulary rows per logit tile of the dz recompute (256,
+ *                      or 128 from N = 2^22 on)
+ * Every logit tile is 256 tokens wide.
  */
-#define FLCE_PLAN_FIELDS 13
+#define FLCE_PLAN_FIELDS 15
 int flce_plan_info(const flce_problem* p, int64_t* out, int n_out);
 
 /* Description of the last error on this thread ("" if none). */

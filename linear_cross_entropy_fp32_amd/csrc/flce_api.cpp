@@ -37,11 +37,12 @@ constexpr int64_t kMaxElems = int64_t(1) << 31;      // V*H stays int32-indexabl
 constexpr int64_t kMaxOperandBytes = (int64_t(1) << 31) - 1;
 constexpr size_t kAlign = 256;
 constexpr int64_t kTargetWgs = 2048;                 // forward workgroups: ~8 per CU
-constexpr int64_t kDzWgs = 256 * kLogitWgsPerCu;     // dz workgroups per chunk: one round
+constexpr int64_t kDzWgs = 256;                      // dz workgroups per chunk: one round (one per CU)
 // ... unless that would give a workgroup more vocab tiles than this (at N =
 // 16384 with 16384-row chunks: 8 tiles in two rounds measured 1% faster than
 // 16 in one)
 constexpr int64_t kMaxDzTilesPerWg = 8;
+constexpr int64_t kDzOneTileHidden = 4096;
 constexpr int64_t kMaxGhSplits = 32;                  // grad_hidden split-K slots
 // bf16 dz of one backward vocab chunk.  A 128 MiB chunk stays in the 256 MB
 // last-level cache (MALL) between the dz write and the contraction's two
@@ -62,15 +63,19 @@ constexpr int64_t kMinChunkWidth = 8192;
 constexpr int64_t kMaxChunkRows = int64_t(1) << 21;
 constexpr int64_t kColsumElems = int64_t(1) << 22;   // fp32 partials of the grad_bias sums
 constexpr int64_t kL2Bytes = int64_t(4) << 20;        // L2 of one XCD
-constexpr int64_t kWindowWgs = 64;                    // logit-tile workgroups one XCD holds
+// logit-tile workgroups one XCD (32 CUs) holds at once: two per CU of the
+// narrow tile, one of the wide
+constexpr int64_t window_wgs(int tile_v) { return tile_v == kWideTileV ? 32 : 64; }
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline int64_t rup(int64_t a, int64_t b) { return cdiv(a, b) * b; }
 inline size_t aup(size_t a) { return (a + kAlign - 1) / kAlign * kAlign; }
 
 struct Plan {
+  int fwd_tile_v;        // vocabulary rows per forward tile (kNarrowTileV or kWideTileV)
+  int dz_tile_v;         // vocabulary rows per dz tile (kNarrowTileV or kWideTileV)
   int n_tok_tiles, n_voc_tiles, n_splits, tiles_per_split, fin_blocks;
-  int64_t vc;            // vocab chunk width of the backward (multiple of the logit tile)
+  int64_t vc;            // vocab chunk width of the backward (multiple of dz_tile_v)
   int n_chunks;
   int dz_tiles_per_wg;   // vocab tiles streamed by one dz workgroup
   int gh_splits;         // split-K of the grad_hidden contraction
@@ -120,9 +125,11 @@ Plan make_plan(const flce_problem* p) {
   Plan pl{};
   const int64_t n = p->n_tokens, h = p->hidden, v = p->vocab;
   pl.n_tok_tiles = (int)cdiv(n, kLogitTileN);
-  pl.n_voc_tiles = (int)cdiv(v, kLogitTileV);
+  pl.fwd_tile_v = h >= kFwdWideMinHidden ? kWideTileV : kNarrowTileV;
+  pl.n_voc_tiles = (int)cdiv(v, pl.fwd_tile_v);
   pl.fin_blocks = (int)cdiv(n, kFinalTokens);
-  const int64_t hidden_bf16_bytes = n * h * 2 * (p->hidden_dtype == FLCE_F32 ? 2 : 1);
+  // the products read one bf16 copy of the hidden states (an fp32 one rounded)
+  const int64_t hidden_bf16_bytes = n * h * 2;
   pl.tt_fastest = hidden_bf16_bytes <= kL2Bytes ? 1 : 0;
   // token tiles per window of the logit-tile order: 8 when the hidden
   // operand fits in L2 anyway; else as many as keep their hidden rows within
@@ -139,7 +146,7 @@ Plan make_plan(const flce_problem* p) {
   // an XCD (fewer splits would put several windows, and their token tiles'
   // hidden rows, on one XCD at once)
   int64_t splits = n > 0 ? cdiv(kTargetWgs, pl.n_tok_tiles) : 1;
-  if (!pl.tt_fastest) splits = std::max<int64_t>(splits, kWindowWgs / pl.win_tt);
+  if (!pl.tt_fastest) splits = std::max<int64_t>(splits, window_wgs(pl.fwd_tile_v) / pl.win_tt);
   splits = std::max<int64_t>(1, std::min<int64_t>(splits, pl.n_voc_tiles));
   pl.tiles_per_split = (int)cdiv(pl.n_voc_tiles, splits);
   pl.n_splits = (int)cdiv(pl.n_voc_tiles, pl.tiles_per_split);
@@ -149,20 +156,22 @@ Plan make_plan(const flce_problem* p) {
   // and at least N rows wide (so a grad_hidden tile's K, the chunk's rows,
   // is never shorter than a grad_weight tile's K, the N tokens), as long as
   // the chunk stays below the 2^31-byte operand limit
-  int64_t vc = n > 0 ? (kDzChunkBytes / (2 * n)) / kLogitTileV * kLogitTileV : rup(v, kLogitTileV);
+  pl.dz_tile_v = n * 2 * kWideTileV <= kMaxOperandBytes ? kWideTileV : kNarrowTileV;
+  const int64_t dt = pl.dz_tile_v;
+  int64_t vc = n > 0 ? (kDzChunkBytes / (2 * n)) / dt * dt : rup(v, dt);
   if (n > 0 && vc < kMinChunkWidth)
-    vc = (kDzChunkBytesWide / (2 * n)) / kLogitTileV * kLogitTileV;
+    vc = (kDzChunkBytesWide / (2 * n)) / dt * dt;
   if (n > 0) {
-    vc = std::max<int64_t>(vc, rup(n, kLogitTileV));
-    vc = std::min<int64_t>(vc, kMaxOperandBytes / (2 * n) / kLogitTileV * kLogitTileV);
+    vc = std::max<int64_t>(vc, rup(n, dt));
+    vc = std::min<int64_t>(vc, kMaxOperandBytes / (2 * n) / dt * dt);
   }
-  vc = std::min<int64_t>(vc, kMaxOperandBytes / (2 * h) / kLogitTileV * kLogitTileV);
+  vc = std::min<int64_t>(vc, kMaxOperandBytes / (2 * h) / dt * dt);
   vc = std::min<int64_t>(vc, kMaxChunkRows);
-  vc = std::max<int64_t>(vc, kLogitTileV);
-  vc = std::min<int64_t>(vc, rup(v, kLogitTileV));
+  vc = std::max<int64_t>(vc, dt);
+  vc = std::min<int64_t>(vc, rup(v, dt));
   pl.vc = vc;
   pl.n_chunks = (int)cdiv(v, vc);
-  const int64_t chunk_tiles = vc / kLogitTileV;
+  const int64_t chunk_tiles = vc / dt;
   // with the row compaction only the valid rows' token tiles have work, so
   // the workgroups take half as many tiles each: twice as many workgroups,
   // which keeps the GPU filled when a third of the rows carry a loss
@@ -174,8 +183,12 @@ Plan make_plan(const flce_problem* p) {
   // hidden rows within half of its L2
   if (!pl.tt_fastest)
     while (pl.dz_tiles_per_wg > 1 &&
-           cdiv(kWindowWgs, cdiv(chunk_tiles, pl.dz_tiles_per_wg)) * tile_bytes > kL2Bytes / 2)
+           cdiv(window_wgs(pl.dz_tile_v), cdiv(chunk_tiles, pl.dz_tiles_per_wg)) * tile_bytes >
+               kL2Bytes / 2)
       pl.dz_tiles_per_wg /= 2;
+  // from H = 4096 on (128 K slices per tile), one tile per workgroup: at
+  // N = 16384, H = 4096 two tiles per workgroup made the step 3% slower
+  if (h >= kDzOneTileHidden) pl.dz_tiles_per_wg = 1;
   // grad_hidden split: its workgroups get twice the K depth of the
   // grad_weight ones (N), but at least 1024; the launch interleaves the two
   // kinds so every XCD gets the same mix, and fewer splits mean fewer partial
@@ -486,7 +499,7 @@ int flce_plan_info(const flce_problem* p, int64_t* out, int n_out) {
   const int64_t v[FLCE_PLAN_FIELDS] = {
       pl.vc, pl.n_chunks, pl.n_splits, pl.tiles_per_split, pl.dz_tiles_per_wg, pl.gh_splits,
       pl.gh_kps, pl.win_tt, pl.tt_fastest, (int64_t)pl.fwd_bytes, (int64_t)pl.bwd_bytes,
-      (int64_t)pl.bytes, p->n_tokens * pl.vc * 2};
+      (int64_t)pl.bytes, p->n_tokens * pl.vc * 2, pl.fwd_tile_v, pl.dz_tile_v};
   const int k = n_out < FLCE_PLAN_FIELDS ? n_out : FLCE_PLAN_FIELDS;
   for (int i = 0; i < k; ++i) out[i] = v[i];
   return k;
@@ -575,6 +588,7 @@ int flce_forward(const flce_problem* p, const void* hidden, const void* weight,
     a.win_tt = pl.win_tt;
     a.tiles_per_split = pl.tiles_per_split;
     a.n_voc_tiles = pl.n_voc_tiles;
+    a.tile_v = pl.fwd_tile_v;
     a.part = part;
     // softcapped logits lie below c: with 2c*log2(e) <= 120 the sums can use
     // the fixed reference c (no running max) without underflowing fp32
@@ -712,7 +726,8 @@ int flce_backward(const flce_problem* p, const void* hidden, const void* weight,
     const int64_t c0 = int64_t(c) * pl.vc;
     const int64_t width = std::min<int64_t>(pl.vc, v - c0);
     d.c0 = (int)c0;
-    d.chunk_tiles = (int)cdiv(width, kLogitTileV);
+    d.tile_v = pl.dz_tile_v;
+    d.chunk_tiles = (int)cdiv(width, pl.dz_tile_v);
     if ((rc = hip_check(timed(FLCE_KERNEL_BWD_DZ, s,
                               [&] { return launch_bwd_dz(d, p->softcap > 0, s); }),
                         "bwd_dz")))

@@ -5,11 +5,23 @@
 
 namespace flce {
 
-// Logit tiles (forward stats, backward dz): 128 vocabulary rows x 256 tokens,
-// four waves in a 2 x 2 grid, two workgroups per CU.
-constexpr int kLogitTileV = 128;
+// Logit tiles (forward stats, backward dz) are 256 tokens wide, and every
+// wave owns 64 vocabulary rows x 128 tokens of one.  Two shapes:
+//  * narrow: 128 vocabulary rows, four waves in a 2 x 2 grid, a three-stage
+//    ring (72 KB of LDS), two workgroups per CU, so that the epilogue of one
+//    overlaps the K loop of the other;
+//  * wide: 256 vocabulary rows, eight waves in a 4 x 2 grid, a four-stage
+//    ring (128 KB), one workgroup per CU: a third fewer L2-to-LDS bytes per
+//    MFMA and three slices in flight instead of two, but the eight waves
+//    reach their epilogues together.
+// The forward takes the wide shape from kFwdWideMinHidden on, where a tile's
+// K loop (H / 32 slices) is long against its epilogue; the dz recompute takes
+// it unless one wide tile's column of dz (N x 256 bf16) would not fit the
+// 2^31-byte extent of a buffer descriptor (N >= 2^22).
 constexpr int kLogitTileN = 256;
-constexpr int kLogitWgsPerCu = 2;
+constexpr int kNarrowTileV = 128;
+constexpr int kWideTileV = 256;
+constexpr int kFwdWideMinHidden = 1024;
 // Contraction tiles (grad_hidden, grad_weight): 256 x 128 outputs.
 constexpr int kGemmTileM = 256;
 constexpr int kGemmTileN = 128;
@@ -36,6 +48,7 @@ struct FwdArgs {
   const int64_t* tgt;    // [N]
   int n, hdim, v;
   float kx, c1, c2;      // see final_u()
+  int tile_v;            // vocabulary rows per tile: kNarrowTileV or kWideTileV
   int n_tok_tiles, n_splits, tiles_per_split, n_voc_tiles;
   int tt_fastest;        // workgroup order (see grouped_order)
   int win_tt;            // token tiles per workgroup window (see grouped_order)
@@ -82,7 +95,8 @@ struct DzArgs {
   int64_t ignore_index;
   float kx, c1, c2;
   int c0;                // first vocab row of the chunk
-  int chunk_tiles;       // vocab tiles in the chunk
+  int tile_v;            // vocabulary rows per tile: kNarrowTileV or kWideTileV
+  int chunk_tiles;       // vocab tiles (tile_v rows) in the chunk
   int tiles_per_wg;      // vocab tiles streamed by one workgroup
   int n_tok_tiles;
   int tt_fastest;        // workgroup order (see grouped_order)

@@ -27,14 +27,28 @@ constexpr float kNegInf = -__builtin_huge_valf();
 constexpr float kMasked = -3.0e38f;
 
 static_assert(kSliceK == kBK, "slice depth");
-static_assert(4 * 32 * (kLogitTileV / 2) * 2 <= Tile<kLogitTileV, kLogitTileN, true, true>::kStage,
-              "dz transpose buffer fits one LDS stage");
-using LogitTile = Tile<kLogitTileV, kLogitTileN, true, true>;
+// The two logit tile shapes (see kNarrowTileV / kWideTileV).  Both give a
+// wave the same 64 x 128 block, so the epilogues are shared; both keep two
+// waves on every SIMD (8 waves per CU).
+using NarrowTile = Tile<kNarrowTileV, kLogitTileN, true, true, 2, 2, 3>;
+using WideTile = Tile<kWideTileV, kLogitTileN, true, true, 4, 2, 4>;
 using GhTile = Tile<kGemmTileM, kGemmTileN, true, false>;          // dz . W
 using GwTile = Tile<kGemmTileM, kGemmTileN, false, false>;         // dz^T . h
-constexpr int kColumns = LogitTile::TN;      // token columns per lane
-constexpr int kQ = LogitTile::TM * 16;       // values per token column per lane
-constexpr int kWaveRows = kLogitTileV / 2;   // vocabulary rows per wave
+constexpr int kColumns = NarrowTile::TN;     // token columns per lane
+constexpr int kQ = NarrowTile::TM * 16;      // values per token column per lane
+constexpr int kWaveRows = 64;                // vocabulary rows per wave
+static_assert(WideTile::TM == NarrowTile::TM && WideTile::TN == NarrowTile::TN &&
+                  kNarrowTileV / NarrowTile::kWM == kWaveRows &&
+                  kWideTileV / WideTile::kWM == kWaveRows,
+              "one wave block in both logit tile shapes");
+static_assert(WideTile::kWaves * 32 * kWaveRows * 2 <= WideTile::kStage &&
+                  NarrowTile::kWaves * 32 * kWaveRows * 2 <= NarrowTile::kStage,
+              "dz transpose buffer fits one LDS stage");
+template <class LT>
+constexpr int wgs_per_cu() { return 8 / LT::kWaves; }
+// workgroups one XCD (32 CUs) holds at once: the window of grouped_order
+template <class LT>
+constexpr int window_wgs() { return 32 * wgs_per_cu<LT>(); }
 
 // ------------------------------------------------------------------ helpers
 
@@ -130,8 +144,9 @@ __device__ __forceinline__ void bias4(const float* blk, int a, int half, float (
 }
 
 // The wave's 64-value block of tile t in the row-DMA buffers at `rows`.
+template <class LT>
 __device__ __forceinline__ const float* bias_block(const float* rows, int t) {
-  return rows + (t % kRowDmaBufs) * 256 + (threadIdx.x >> 6) * 64;
+  return rows + (t % LT::kRing) * (LT::kWaves * 64) + (threadIdx.x >> 6) * 64;
 }
 
 // ------------------------------------------- fp32 operands: rounded to bf16
@@ -390,7 +405,7 @@ __device__ __forceinline__ void fold_column(float (&val)[kQ], PartState& st, int
   }
 }
 
-template <bool CAP, bool FIXED, bool BIAS>
+template <class LT, bool CAP, bool FIXED, bool BIAS>
 struct FwdEpilogue {
   static constexpr bool kUsesLds = false;
   const FwdArgs& a;
@@ -399,11 +414,11 @@ struct FwdEpilogue {
   const float* rows;               // row-DMA buffers of the bias (BIAS)
   int vt_begin, wm, half;
 
-  __device__ __forceinline__ void operator()(int t, LogitTile& T, char*) {
-    const int v0 = (vt_begin + t) * kLogitTileV;
+  __device__ __forceinline__ void operator()(int t, LT& T, char*) {
+    const int v0 = (vt_begin + t) * LT::kBM;
     const int vw = v0 + wm * kWaveRows;
-    const bool tail = v0 + kLogitTileV > a.v;
-    const float* blk = BIAS ? bias_block(rows, t) : nullptr;
+    const bool tail = v0 + LT::kBM > a.v;
+    const float* blk = BIAS ? bias_block<LT>(rows, t) : nullptr;
 #pragma unroll
     for (int j = 0; j < kColumns; ++j) {
       // the bias values are read again for every column, four at a time, so
@@ -441,44 +456,44 @@ struct FwdEpilogue {
 // One workgroup = one token tile x one contiguous range ("split") of vocab
 // tiles, streamed through the tile engine; each finished logit tile is folded
 // into the per-token states held in registers.  At the end of the split the
-// states of the two half-waves and of the two waves sharing a token are merged
+// states of the two half-waves and of the waves sharing a token are merged
 // and written as one partial state per (split, token).
-template <bool CAP, bool FIXED, bool BIAS>
-__global__ void __launch_bounds__(kThreads, kLogitWgsPerCu)
+template <class LT, bool CAP, bool FIXED, bool BIAS>
+__global__ void __launch_bounds__(LT::kThr, wgs_per_cu<LT>())
 fwd_stats_kernel(const FwdArgs a) {
-  __shared__ __attribute__((aligned(16))) char lds[LogitTile::kLdsBytes];
+  __shared__ __attribute__((aligned(16))) char lds[LT::kLdsBytes];
   const GridPos gp =
       grouped_order(xcd_remap(blockIdx.x, gridDim.x), a.n_tok_tiles, a.n_splits, a.win_tt,
-                    a.tt_fastest);
+                    a.tt_fastest, window_wgs<LT>());
   const int tt = gp.tt, sp = gp.grp;
   const int n0 = tt * kLogitTileN;
   const int n_rows = a.n_dev ? *a.n_dev : a.n;   // rows computed (compacted rows first)
   if (n0 >= n_rows) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave & 1, wn = wave >> 1;
+  const int wm = wave % LT::kWM, wn = wave / LT::kWM;
   const int half = lane >> 5;
 
   int tgt[kColumns];
   PartState st[kColumns];
 #pragma unroll
   for (int j = 0; j < kColumns; ++j) {
-    const int n = n0 + wn * (kLogitTileN / 2) + j * 32 + (lane & 31);
+    const int n = n0 + wn * (kLogitTileN / LT::kWN) + j * 32 + (lane & 31);
     const int64_t t = (n < n_rows) ? a.tgt[a.perm ? a.perm[n] : n] : -1;
     tgt[j] = (t >= 0 && t < a.v) ? (int)t : -(1 << 30);
     st[j] = PartState{FIXED ? 0.f : kNegInf, 0.f, 0.f, kNegInf, kNegInf, 0x7fffffff};
   }
   const int vt_begin = sp * a.tiles_per_split;
   const int ntiles = min(a.n_voc_tiles, vt_begin + a.tiles_per_split) - vt_begin;
-  const Operand opA{a.w, a.hdim, vt_begin * kLogitTileV, a.v, a.hdim};
+  const Operand opA{a.w, a.hdim, vt_begin * LT::kBM, a.v, a.hdim};
   const Operand opB{a.h0, a.hdim, n0, n_rows, a.hdim};
-  __shared__ __attribute__((aligned(16))) float rows[BIAS ? kRowDmaBytes / 4 : 4];
+  __shared__ __attribute__((aligned(16))) float rows[BIAS ? LT::kRowDmaBytes / 4 : 4];
   RowDma rd{};
   if constexpr (BIAS)
     rd = RowDma{dma_rsrc(a.bias, (int64_t)a.v * 4), lds_addr(reinterpret_cast<char*>(rows)),
-                vt_begin * kLogitTileV};
-  FwdEpilogue<CAP, FIXED, BIAS> epi{a, st, tgt, rows, vt_begin, wm, half};
-  LogitTile T;
-  T.run_stream<BIAS>(lds, opA, opB, a.hdim, ntiles, epi, rd);
+                vt_begin * LT::kBM};
+  FwdEpilogue<LT, CAP, FIXED, BIAS> epi{a, st, tgt, rows, vt_begin, wm, half};
+  LT T;
+  T.template run_stream<BIAS>(lds, opA, opB, a.hdim, ntiles, epi, rd);
 
 #pragma unroll
   for (int j = 0; j < kColumns; ++j) {
@@ -491,17 +506,25 @@ fwd_stats_kernel(const FwdArgs a) {
     }
     st[j] = merge_state(st[j], shfl_xor_state(st[j], 32));
   }
+  // the waves wm = 1 .. kWM-1 of a token column hand their states to wave
+  // wm = 0, which merges them in increasing wm (vocabulary) order
   PartState* sh = reinterpret_cast<PartState*>(lds);
-  if (wm == 1 && half == 0) {
+  static_assert((LT::kWM - 1) * LT::kWN * kColumns * 32 * sizeof(PartState) <= LT::kLdsBytes,
+                "merge buffer");
+  if (wm > 0 && half == 0) {
 #pragma unroll
-    for (int j = 0; j < kColumns; ++j) sh[(wn * kColumns + j) * 32 + lane] = st[j];
+    for (int j = 0; j < kColumns; ++j)
+      sh[(((wm - 1) * LT::kWN + wn) * kColumns + j) * 32 + lane] = st[j];
   }
   __syncthreads();
   if (wm == 0 && half == 0) {
 #pragma unroll
     for (int j = 0; j < kColumns; ++j) {
-      const PartState o = merge_state(st[j], sh[(wn * kColumns + j) * 32 + lane]);
-      const int n = n0 + wn * (kLogitTileN / 2) + j * 32 + lane;
+      PartState o = st[j];
+#pragma unroll
+      for (int w = 1; w < LT::kWM; ++w)
+        o = merge_state(o, sh[(((w - 1) * LT::kWN + wn) * kColumns + j) * 32 + lane]);
+      const int n = n0 + wn * (kLogitTileN / LT::kWN) + j * 32 + lane;
       if (n < n_rows) a.part[(int64_t)sp * a.n + n] = o;
     }
   }
@@ -666,7 +689,7 @@ __device__ __forceinline__ float row_grad(const DzArgs& a, int n, int64_t t) {
   return g * a.scale;
 }
 
-template <bool CAP, bool BIAS>
+template <class LT, bool CAP, bool BIAS>
 struct DzEpilogue {
   // The finished tile is transposed through a free LDS stage so that every
   // store covers whole 128-byte rows of dz (8 lanes per token).
@@ -678,12 +701,12 @@ struct DzEpilogue {
   const float* rows;               // row-DMA buffers of the bias (BIAS)
   int vt_begin, wm, half, nbase;   // nbase: first token of the wave's columns
 
-  __device__ __forceinline__ void operator()(int t, LogitTile& T, char* free_lds) {
+  __device__ __forceinline__ void operator()(int t, LT& T, char* free_lds) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int v0 = a.c0 + (vt_begin + t) * kLogitTileV;
+    const int v0 = a.c0 + (vt_begin + t) * LT::kBM;
     const int vw = __builtin_amdgcn_readfirstlane(v0 + wm * kWaveRows);
-    const bool tail = v0 + kLogitTileV > a.v;
-    const float* blk = BIAS ? bias_block(rows, t) : nullptr;
+    const bool tail = v0 + LT::kBM > a.v;
+    const float* blk = BIAS ? bias_block<LT>(rows, t) : nullptr;
     // [32 tokens][64 vocabulary rows] bf16 of this wave; the 8-byte piece p of
     // token row tl is stored at piece p ^ (tl / 2), which keeps both the
     // 8-byte writes and the 16-byte reads below free of bank conflicts
@@ -775,27 +798,27 @@ struct DzEpilogue {
   }
 };
 
-template <bool CAP, bool BIAS>
-__global__ void __launch_bounds__(kThreads, kLogitWgsPerCu)
+template <class LT, bool CAP, bool BIAS>
+__global__ void __launch_bounds__(LT::kThr, wgs_per_cu<LT>())
 bwd_dz_kernel(const DzArgs a) {
-  __shared__ __attribute__((aligned(16))) char lds[LogitTile::kLdsBytes];
+  __shared__ __attribute__((aligned(16))) char lds[LT::kLdsBytes];
   const int groups = (a.chunk_tiles + a.tiles_per_wg - 1) / a.tiles_per_wg;
   const GridPos gp =
       grouped_order(xcd_remap(blockIdx.x, gridDim.x), a.n_tok_tiles, groups, a.win_tt,
-                    a.tt_fastest);
+                    a.tt_fastest, window_wgs<LT>());
   const int tt = gp.tt, grp = gp.grp;
   const int n0 = tt * kLogitTileN;
   const int n_rows = a.n_dev ? *a.n_dev : a.n;   // rows computed (compacted rows first)
   if (n0 >= n_rows) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave & 1, wn = wave >> 1;
+  const int wm = wave % LT::kWM, wn = wave / LT::kWM;
   const int half = lane >> 5;
 
   float gs[kColumns], nl[kColumns];
   int tgt[kColumns];
 #pragma unroll
   for (int j = 0; j < kColumns; ++j) {
-    const int n = n0 + wn * (kLogitTileN / 2) + j * 32 + (lane & 31);
+    const int n = n0 + wn * (kLogitTileN / LT::kWN) + j * 32 + (lane & 31);
     const bool in = n < n_rows;
     const int row = in ? (a.perm ? a.perm[n] : n) : 0;
     const int64_t t = in ? a.tgt[row] : -1;
@@ -805,17 +828,17 @@ bwd_dz_kernel(const DzArgs a) {
   }
   const int vt_begin = grp * a.tiles_per_wg;
   const int ntiles = min(a.chunk_tiles, vt_begin + a.tiles_per_wg) - vt_begin;
-  const Operand opA{a.w, a.hdim, a.c0 + vt_begin * kLogitTileV, a.v, a.hdim};
+  const Operand opA{a.w, a.hdim, a.c0 + vt_begin * LT::kBM, a.v, a.hdim};
   const Operand opB{a.h0, a.hdim, n0, n_rows, a.hdim};
-  __shared__ __attribute__((aligned(16))) float rows[BIAS ? kRowDmaBytes / 4 : 4];
+  __shared__ __attribute__((aligned(16))) float rows[BIAS ? LT::kRowDmaBytes / 4 : 4];
   RowDma rd{};
   if constexpr (BIAS)
     rd = RowDma{dma_rsrc(a.bias, (int64_t)a.v * 4), lds_addr(reinterpret_cast<char*>(rows)),
-                a.c0 + vt_begin * kLogitTileV};
-  DzEpilogue<CAP, BIAS> epi{a, gs, nl, tgt, rows, vt_begin, wm, half,
-                           __builtin_amdgcn_readfirstlane(n0 + wn * (kLogitTileN / 2))};
-  LogitTile T;
-  T.run_stream<BIAS>(lds, opA, opB, a.hdim, ntiles, epi, rd);
+                a.c0 + vt_begin * LT::kBM};
+  DzEpilogue<LT, CAP, BIAS> epi{a, gs, nl, tgt, rows, vt_begin, wm, half,
+                               __builtin_amdgcn_readfirstlane(n0 + wn * (kLogitTileN / LT::kWN))};
+  LT T;
+  T.template run_stream<BIAS>(lds, opA, opB, a.hdim, ntiles, epi, rd);
 }
 
 // ------------------------------------------- contractions over a dz chunk
@@ -1009,11 +1032,11 @@ hipError_t launch_target_logits(const TargetArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_fwd_stats(const FwdArgs& a, bool cap, bool fixed_ref, hipStream_t s) {
-  const unsigned grid = (unsigned)(a.n_tok_tiles * a.n_splits);
-  if (grid == 0) return hipSuccess;
+template <class LT>
+static void launch_fwd_shape(const FwdArgs& a, bool cap, bool fixed_ref, unsigned grid,
+                             hipStream_t s) {
   const bool bias = a.bias != nullptr;
-#define FLCE_FWD(C, F, B) fwd_stats_kernel<C, F, B><<<grid, kThreads, 0, s>>>(a)
+#define FLCE_FWD(C, F, B) fwd_stats_kernel<LT, C, F, B><<<grid, LT::kThr, 0, s>>>(a)
   if (cap && fixed_ref) {
     if (bias) FLCE_FWD(true, true, true); else FLCE_FWD(true, true, false);
   } else if (cap) {
@@ -1022,6 +1045,17 @@ hipError_t launch_fwd_stats(const FwdArgs& a, bool cap, bool fixed_ref, hipStrea
     if (bias) FLCE_FWD(false, false, true); else FLCE_FWD(false, false, false);
   }
 #undef FLCE_FWD
+}
+
+hipError_t launch_fwd_stats(const FwdArgs& a, bool cap, bool fixed_ref, hipStream_t s) {
+  const unsigned grid = (unsigned)(a.n_tok_tiles * a.n_splits);
+  if (grid == 0) return hipSuccess;
+  if (a.tile_v == kWideTileV)
+    launch_fwd_shape<WideTile>(a, cap, fixed_ref, grid, s);
+  else if (a.tile_v == kNarrowTileV)
+    launch_fwd_shape<NarrowTile>(a, cap, fixed_ref, grid, s);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
@@ -1034,18 +1068,28 @@ hipError_t launch_fwd_finalize(const FinalArgs& a, int nblocks, float mean_divis
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_dz(const DzArgs& a, bool cap, hipStream_t s) {
-  const int groups = (a.chunk_tiles + a.tiles_per_wg - 1) / a.tiles_per_wg;
-  const unsigned grid = (unsigned)(a.n_tok_tiles * groups);
-  if (grid == 0) return hipSuccess;
+template <class LT>
+static void launch_dz_shape(const DzArgs& a, bool cap, unsigned grid, hipStream_t s) {
   const bool bias = a.bias != nullptr;
-#define FLCE_DZ(C, B) bwd_dz_kernel<C, B><<<grid, kThreads, 0, s>>>(a)
+#define FLCE_DZ(C, B) bwd_dz_kernel<LT, C, B><<<grid, LT::kThr, 0, s>>>(a)
   if (cap) {
     if (bias) FLCE_DZ(true, true); else FLCE_DZ(true, false);
   } else {
     if (bias) FLCE_DZ(false, true); else FLCE_DZ(false, false);
   }
 #undef FLCE_DZ
+}
+
+hipError_t launch_bwd_dz(const DzArgs& a, bool cap, hipStream_t s) {
+  const int groups = (a.chunk_tiles + a.tiles_per_wg - 1) / a.tiles_per_wg;
+  const unsigned grid = (unsigned)(a.n_tok_tiles * groups);
+  if (grid == 0) return hipSuccess;
+  if (a.tile_v == kWideTileV)
+    launch_dz_shape<WideTile>(a, cap, grid, s);
+  else if (a.tile_v == kNarrowTileV)
+    launch_dz_shape<NarrowTile>(a, cap, grid, s);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

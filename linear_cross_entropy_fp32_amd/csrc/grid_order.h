@@ -13,18 +13,18 @@
 namespace flce {
 
 // Order over a (token tile, vocabulary group) grid in windows of up to
-// G groups x T token tiles, G = 64 / T (64 workgroups: what one XCD holds at
-// two per CU; T a power of two).  Inside a window, consecutive workgroups
-// share the operand that benefits most from being read by workgroups that
-// run in step: the vocabulary group (token tile fastest) when all token
+// G groups x T token tiles, G = W / T (W workgroups: what one XCD holds at
+// once, 32 x the workgroups per CU; W and T powers of two, T <= W).  Inside
+// a window, consecutive workgroups share the operand that benefits most from
+// being read by workgroups that run in step: the vocabulary group (token tile fastest) when all token
 // tiles fit in L2 anyway, else the token tile (group fastest).  Windows run
 // over the token tiles of a band of G groups, then the next band; edge
 // windows are narrower.  The map is a bijection onto the n_tt x n_grp grid.
 struct GridPos {
   int tt, grp;
 };
-FLCE_HD inline GridPos grouped_order(int id, int n_tt, int n_grp, int T, bool tt_fastest) {
-  const int G = 64 / T;
+FLCE_HD inline GridPos grouped_order(int id, int n_tt, int n_grp, int T, bool tt_fastest, int W) {
+  const int G = W / T;
   const int b = id / (n_tt * G), r = id - b * (n_tt * G);
   const int gh = n_grp - b * G < G ? n_grp - b * G : G;    // groups in this band
   const int tb = r / (T * gh), j = r - tb * (T * gh);

@@ -157,11 +157,13 @@ __device__ __forceinline__ void dma4_at(const u32x4& rs, uint32_t m0, uint32_t o
 // the tile's epilogue is done (the issue pointer runs two slices ahead).
 struct RowDma {
   u32x4 rsrc;      // 4-byte values per A row; rows past its size read zero
-  uint32_t lds;    // LDS byte address of buffer 0 (kRowDmaBufs x 1 KB)
+  uint32_t lds;    // LDS byte address of buffer 0 (row_dma_bytes(...))
   int row0;        // A row of the first tile
 };
-constexpr int kRowDmaBufs = 3;
-constexpr int kRowDmaBytes = kRowDmaBufs * 4 * 256;
+// Row-DMA buffers: one per ring stage (the issue pointer runs STAGES - 1
+// slices ahead, so a one-slice tile's buffer is reloaded STAGES tiles later,
+// after its epilogue), each one 256-byte block per wave.
+constexpr int row_dma_bytes(int stages, int waves) { return stages * waves * 256; }
 
 // LDS byte address of a pointer into the workgroup's LDS array.
 __device__ __forceinline__ uint32_t lds_addr(const char* p) {
@@ -204,15 +206,15 @@ __device__ __forceinline__ void lds_barrier() {
 
 // --------------------------------------------------------------- operands
 
-template <int R, bool KMAJ>
+template <int R, bool KMAJ, int NW>
 struct Stage;
 
-template <int R>
-struct Stage<R, true> {
+template <int R, int NW>
+struct Stage<R, true, NW> {
   static constexpr int kRowBytes = kBK * 2;                 // 64
   static constexpr int kBytes = R * kRowBytes;
-  static constexpr int kPerWave = R * (kBK / 8) / 4 / 64;   // DMA instructions per wave
-  static_assert(kPerWave >= 1 && R % 64 == 0, "K-major tile shape");
+  static constexpr int kPerWave = R * (kBK / 8) / NW / 64;  // DMA instructions per wave
+  static_assert(kPerWave >= 1 && kPerWave * NW * 64 == R * (kBK / 8), "K-major tile shape");
   __device__ static __forceinline__ int swz(int r) { return (r >> 2) & 3; }
 
   struct Src {
@@ -277,13 +279,15 @@ struct Stage<R, true> {
   }
 };
 
-template <int R>
-struct Stage<R, false> {
+template <int R, int NW>
+struct Stage<R, false, NW> {
   static constexpr int kRowBytes = R * 2;                   // one K row
   static constexpr int kBytes = kBK * kRowBytes;
   static constexpr int kCPR = R / 8;                        // chunks per K row
-  static constexpr int kPerWave = kBK * kCPR / 4 / 64;
-  static_assert(kPerWave >= 1 && kCPR >= 16 && kCPR % 16 == 0, "MN-major tile shape");
+  static constexpr int kPerWave = kBK * kCPR / NW / 64;
+  static_assert(kPerWave >= 1 && kPerWave * NW * 64 == kBK * kCPR && kCPR >= 16 &&
+                    kCPR % 16 == 0,
+                "MN-major tile shape");
   __device__ static __forceinline__ int swz(int k) { return (k & 3) << 2; }
 
   struct Src {
@@ -358,15 +362,19 @@ struct Stage<R, false> {
 
 // ------------------------------------------------------------------- tile
 
-template <int BM, int BN, bool A_KMAJ, bool B_KMAJ>
+template <int BM, int BN, bool A_KMAJ, bool B_KMAJ, int WM = 2, int WN = 2, int STAGES = kStages>
 struct Tile {
   static constexpr int kBM = BM, kBN = BN;
-  static constexpr int TM = BM / 64, TN = BN / 64;
-  using SA = Stage<BM, A_KMAJ>;
-  using SB = Stage<BN, B_KMAJ>;
+  static constexpr int kWM = WM, kWN = WN, kWaves = WM * WN, kThr = 64 * WM * WN;
+  static constexpr int kRing = STAGES;
+  static constexpr int TM = BM / WM / 32, TN = BN / WN / 32;
+  static_assert(TM * WM * 32 == BM && TN * WN * 32 == BN, "wave grid");
+  using SA = Stage<BM, A_KMAJ, WM * WN>;
+  using SB = Stage<BN, B_KMAJ, WM * WN>;
   static constexpr int kLdsA = SA::kBytes;
   static constexpr int kStage = SA::kBytes + SB::kBytes;
-  static constexpr int kLdsBytes = kStages * kStage;
+  static constexpr int kLdsBytes = STAGES * kStage;
+  static constexpr int kRowDmaBytes = row_dma_bytes(STAGES, WM * WN);
   static constexpr int kLoads = SA::kPerWave + SB::kPerWave;   // per wave per slice
 
   f32x16 acc[TM][TN];
@@ -385,14 +393,14 @@ struct Tile {
   template <bool FIRST = false>
   __device__ __forceinline__ void mma_stage(const char* lds) {
     const int wave = threadIdx.x >> 6;
-    const int wm = wave & 1, wn = wave >> 1;
+    const int wm = wave % WM, wn = wave / WM;
 #pragma unroll
     for (int ks = 0; ks < kBK / 16; ++ks) {
       bf16x8 fa[TM], fb[TN];
 #pragma unroll
-      for (int j = 0; j < TN; ++j) fb[j] = SB::frag(lds + kLdsA, wn * (BN / 2) + j * 32, ks);
+      for (int j = 0; j < TN; ++j) fb[j] = SB::frag(lds + kLdsA, wn * (BN / WN) + j * 32, ks);
 #pragma unroll
-      for (int i = 0; i < TM; ++i) fa[i] = SA::frag(lds, wm * (BM / 2) + i * 32, ks);
+      for (int i = 0; i < TM; ++i) fa[i] = SA::frag(lds, wm * (BM / WM) + i * 32, ks);
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -411,11 +419,11 @@ struct Tile {
   __device__ __forceinline__ static void frags(const char* stage, int ks, bf16x8 (&fa)[TM],
                                                bf16x8 (&fb)[TN]) {
     const int wave = threadIdx.x >> 6;
-    const int wm = wave & 1, wn = wave >> 1;
+    const int wm = wave % WM, wn = wave / WM;
 #pragma unroll
-    for (int j = 0; j < TN; ++j) fb[j] = SB::frag(stage + kLdsA, wn * (BN / 2) + j * 32, ks);
+    for (int j = 0; j < TN; ++j) fb[j] = SB::frag(stage + kLdsA, wn * (BN / WN) + j * 32, ks);
 #pragma unroll
-    for (int i = 0; i < TM; ++i) fa[i] = SA::frag(stage, wm * (BM / 2) + i * 32, ks);
+    for (int i = 0; i < TM; ++i) fa[i] = SA::frag(stage, wm * (BM / WM) + i * 32, ks);
   }
   __device__ __forceinline__ void mma(const bf16x8 (&fa)[TM], const bf16x8 (&fb)[TN]) {
 #pragma unroll
@@ -440,6 +448,7 @@ struct Tile {
   // the wait counts the same in every iteration.
   __device__ __forceinline__ void run(char* lds, const Operand a_op, const Operand b_op,
                                       int k_begin, int k_end) {
+    static_assert(STAGES == 3, "the single-tile loop keeps three slices in flight");
     const int kt_total = (k_end - k_begin + kBK - 1) / kBK;
     if (kt_total <= 0) return;
     const typename SA::Plan a = SA::plan(a_op);
@@ -490,7 +499,7 @@ struct Tile {
   __device__ __forceinline__ void run_stream(char* lds, const Operand a_op, const Operand b_op,
                                              int k_end, int ntiles, Epi& epi,
                                              const RowDma& rd = RowDma{}) {
-    static_assert(!ROWS || BM == 128, "row values: 64 rows per wave");
+    static_assert(!ROWS || BM == 64 * WM, "row values: 64 rows per wave");
     const int kt_tile = (k_end + kBK - 1) / kBK;
     if (kt_tile <= 0 || ntiles <= 0) return;
     const typename SB::Src b = SB::source(b_op);
@@ -505,14 +514,14 @@ struct Tile {
       if constexpr (ROWS) {
         if (is == 0 && it < ntiles) {
           const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-          const int row = rd.row0 + it * BM + (wave & 1) * 64 + (int)(threadIdx.x & 63);
-          dma4_at(rd.rsrc, rd.lds + ibuf * 1024 + wave * 256, (uint32_t)row * 4);
-          ibuf = ibuf == kRowDmaBufs - 1 ? 0 : ibuf + 1;
+          const int row = rd.row0 + it * BM + (wave % WM) * 64 + (int)(threadIdx.x & 63);
+          dma4_at(rd.rsrc, rd.lds + ibuf * (kWaves * 256) + wave * 256, (uint32_t)row * 4);
+          ibuf = ibuf == STAGES - 1 ? 0 : ibuf + 1;
         }
       }
       SA::issue(a, buf, k0);
       SB::issue(b, buf + kLdsA, k0);
-      islot = islot == kStages - 1 ? 0 : islot + 1;
+      islot = islot == STAGES - 1 ? 0 : islot + 1;
       if (++is == kt_tile) {
         is = 0;
         if (++it < ntiles) {
@@ -521,19 +530,20 @@ struct Tile {
         }
       }
     };
-    issue_next();
-    issue_next();
+#pragma unroll
+    for (int i = 0; i < STAGES - 1; ++i) issue_next();
     int cslot = 0;   // ring stage being multiplied
+    constexpr int kAhead = (STAGES - 2) * kLoads;   // loads of later slices left in flight
     for (int ct = 0; ct < ntiles; ++ct) {
       // the first slice of a tile starts the accumulators from zero, so they
       // are dead between the previous epilogue and here
-      vm_barrier<kLoads>();
+      vm_barrier<kAhead>();
       __builtin_amdgcn_s_setprio(kLoopPriority);
       issue_next();
       mma_stage<true>(lds + cslot * kStage);
       for (int cs = 1; cs < kt_tile; ++cs) {
-        cslot = cslot == kStages - 1 ? 0 : cslot + 1;
-        vm_barrier<kLoads>();
+        cslot = cslot == STAGES - 1 ? 0 : cslot + 1;
+        vm_barrier<kAhead>();
         issue_next();
         mma_stage(lds + cslot * kStage);
       }
@@ -544,7 +554,7 @@ struct Tile {
         free_lds = lds + cslot * kStage;
       }
       epi(ct, *this, free_lds);
-      cslot = cslot == kStages - 1 ? 0 : cslot + 1;
+      cslot = cslot == STAGES - 1 ? 0 : cslot + 1;
     }
     vm_barrier<0>();
   }

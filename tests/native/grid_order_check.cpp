@@ -1,6 +1,7 @@
 // Host check of the workgroup orders the kernels use (grid_order.h, the same
 // functions, compiled for the host): for every window size the planner picks
-// (T = 1, 2, 4, 8 token tiles x 64/T vocabulary groups), both inner orders and
+// (windows of W = 32 or 64 workgroups, T = 1, 2, 4, 8 token tiles x W/T
+// vocabulary groups), both inner orders and
 // a spread of grid shapes, grouped_order maps the workgroup ids one to one
 // onto the token-tile x group grid, and xcd_remap is a permutation of the ids.
 // A map that missed or repeated a cell would leave logits unreduced or make a
@@ -24,22 +25,23 @@ int main() {
   shapes.push_back({3, 71});
   shapes.push_back({128, 1187});   // 16384 tokens, 151936 / 128 vocabulary tiles
   long cases = 0;
-  for (int T = 1; T <= 8; T *= 2)
-    for (int fast = 0; fast < 2; ++fast)
-      for (auto [n_tt, n_grp] : shapes) {
-        std::vector<char> seen((size_t)n_tt * n_grp, 0);
-        for (int id = 0; id < n_tt * n_grp; ++id) {
-          const flce::GridPos p = flce::grouped_order(id, n_tt, n_grp, T, fast != 0);
-          if (p.tt < 0 || p.tt >= n_tt || p.grp < 0 || p.grp >= n_grp ||
-              seen[(size_t)p.tt * n_grp + p.grp]) {
-            std::printf("grouped_order fails: T=%d fast=%d n_tt=%d n_grp=%d id=%d\n", T, fast,
-                        n_tt, n_grp, id);
-            return 1;
+  for (int W = 32; W <= 64; W *= 2)
+    for (int T = 1; T <= 8; T *= 2)
+      for (int fast = 0; fast < 2; ++fast)
+        for (auto [n_tt, n_grp] : shapes) {
+          std::vector<char> seen((size_t)n_tt * n_grp, 0);
+          for (int id = 0; id < n_tt * n_grp; ++id) {
+            const flce::GridPos p = flce::grouped_order(id, n_tt, n_grp, T, fast != 0, W);
+            if (p.tt < 0 || p.tt >= n_tt || p.grp < 0 || p.grp >= n_grp ||
+                seen[(size_t)p.tt * n_grp + p.grp]) {
+              std::printf("grouped_order fails: W=%d T=%d fast=%d n_tt=%d n_grp=%d id=%d\n", W,
+                          T, fast, n_tt, n_grp, id);
+              return 1;
+            }
+            seen[(size_t)p.tt * n_grp + p.grp] = 1;
           }
-          seen[(size_t)p.tt * n_grp + p.grp] = 1;
+          ++cases;
         }
-        ++cases;
-      }
   for (int nb = 1; nb <= 5000; nb += (nb < 300 ? 1 : 97)) {
     std::vector<char> seen(nb, 0);
     for (int b = 0; b < nb; ++b) {

@@ -59,6 +59,9 @@ SMALL = [
     # tile, at least 64 forward splits, and (fp32) one dz tile per workgroup
     synth.small_workload(600, 4096, 9000, 41, softcap=30.0, bias=True),
     synth.small_workload(2000, 4096, 16500, 42, hidden_dtype="f32", reduction="none"),
+    # H = 1024, where the forward takes 256-row tiles; running-max softcap path
+    synth.small_workload(700, 1024, 5000, 43, softcap=50.0, logit_scale=2.0, bias=True,
+                         reduction="none"),
 ]
 
 

@@ -7,7 +7,8 @@ Offsets the kernels form in 32 bits (the operand's descriptor base is the
 tile's first row, so a tile adds at most its own rows):
   * dz stores of the recompute kernel: token row (up to 127 past a wave's
     base, phantom rows past N included) x 2 Vc bytes + the column offset;
-  * K-major operand rows of a tile (up to 255 rows): row x 2 ld, with ld = H
+  * K-major operand rows of a tile (up to 255 rows: 256 tokens, or the 128
+    or 256 vocabulary rows of a logit tile): row x 2 ld, with ld = H
     (lm_head, hidden) or Vc (a dz chunk);
   * MN-major operands: K row x 2 ld bytes, K rows running up to the K bound
     plus one 32-deep slice (phantom rows read zero only if the offset does not
@@ -51,7 +52,11 @@ def test_offsets_stay_in_32_bits(chunk):
         pl = flce.flce_plan_info(p)
         vc = pl["chunk_rows"]
         label = (n, h, v, p.hidden_dtype, p.weight_dtype, p.compact_valid, vc)
-        assert vc % 128 == 0 and vc >= 128, label
+        # 256-row logit tiles, except where the operand or dz extent needs 128
+        dt = pl["dz_tile_rows"]
+        assert dt == (256 if n * 2 * 256 < U31 else 128), label
+        assert pl["fwd_tile_rows"] == (256 if h >= 1024 else 128), label
+        assert vc % dt == 0 and vc >= dt, label
         assert pl["n_chunks"] == -(-v // vc), label
         width = min(vc, v)
         # dz stores: 128 token rows of a wave, 2 Vc bytes each
@@ -70,7 +75,7 @@ def test_offsets_stay_in_32_bits(chunk):
         assert pl["gh_splits"] * pl["gh_rows_per_split"] >= width, label
         assert (pl["gh_splits"] - 1) * pl["gh_rows_per_split"] < width, label
         # forward splits cover the vocabulary tiles
-        tiles = -(-v // 128)
+        tiles = -(-v // pl["fwd_tile_rows"])
         assert pl["fwd_splits"] * pl["fwd_tiles_per_split"] >= tiles, label
         assert (pl["fwd_splits"] - 1) * pl["fwd_tiles_per_split"] < tiles, label
 
