@@ -265,9 +265,11 @@ int flce_ce_backward(const flce_ce_problem* p, void* grad_logits, const int64_t*
  *                      256 from H = 1024 on)
  *  14 dz_tile_rows     vocabulary rows per logit tile of the dz recompute (256,
  *                      or 128 from N = 2^22 on)
- * Every logit tile is 256 tokens wide.
+ *  15 contract_tile_cols  output columns per grad_hidden / grad_weight tile
+ *                      (256 when H is a multiple of 256 from 1024 on, else 128)
+ * Every logit tile is 256 tokens wide; every contraction tile 256 rows high.
  */
-#define FLCE_PLAN_FIELDS 15
+#define FLCE_PLAN_FIELDS 16
 int flce_plan_info(const flce_problem* p, int64_t* out, int n_out);
 
 /* Description of the last error on this thread ("" if none). */

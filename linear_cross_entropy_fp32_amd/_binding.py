@@ -27,7 +27,8 @@ EXPORTED = ("flce_validate", "flce_workspace_bytes", "flce_forward", "flce_backw
 PLAN_FIELDS = ("chunk_rows", "n_chunks", "fwd_splits", "fwd_tiles_per_split",
                "dz_tiles_per_wg", "gh_splits", "gh_rows_per_split", "window_token_tiles",
                "token_tile_fastest", "fwd_workspace_bytes", "bwd_workspace_bytes",
-               "workspace_bytes", "dz_chunk_bytes", "fwd_tile_rows", "dz_tile_rows")
+               "workspace_bytes", "dz_chunk_bytes", "fwd_tile_rows", "dz_tile_rows",
+               "contract_tile_cols")
 FLCE_KERNEL_FWD_STATS, FLCE_KERNEL_BWD_DZ, FLCE_KERNEL_CONTRACT = 0, 1, 2
 
 

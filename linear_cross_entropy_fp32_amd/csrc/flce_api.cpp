@@ -74,6 +74,7 @@ inline size_t aup(size_t a) { return (a + kAlign - 1) / kAlign * kAlign; }
 struct Plan {
   int fwd_tile_v;        // vocabulary rows per forward tile (kNarrowTileV or kWideTileV)
   int dz_tile_v;         // vocabulary rows per dz tile (kNarrowTileV or kWideTileV)
+  int gemm_tile_n;       // output columns per contraction tile
   int n_tok_tiles, n_voc_tiles, n_splits, tiles_per_split, fin_blocks;
   int64_t vc;            // vocab chunk width of the backward (multiple of dz_tile_v)
   int n_chunks;
@@ -126,6 +127,8 @@ Plan make_plan(const flce_problem* p) {
   const int64_t n = p->n_tokens, h = p->hidden, v = p->vocab;
   pl.n_tok_tiles = (int)cdiv(n, kLogitTileN);
   pl.fwd_tile_v = h >= kFwdWideMinHidden ? kWideTileV : kNarrowTileV;
+  pl.gemm_tile_n = h >= kContractWideMinHidden && h % kGemmTileNWide == 0 ? kGemmTileNWide
+                                                                         : kGemmTileNNarrow;
   pl.n_voc_tiles = (int)cdiv(v, pl.fwd_tile_v);
   pl.fin_blocks = (int)cdiv(n, kFinalTokens);
   // the products read one bf16 copy of the hidden states (an fp32 one rounded)
@@ -499,7 +502,8 @@ int flce_plan_info(const flce_problem* p, int64_t* out, int n_out) {
   const int64_t v[FLCE_PLAN_FIELDS] = {
       pl.vc, pl.n_chunks, pl.n_splits, pl.tiles_per_split, pl.dz_tiles_per_wg, pl.gh_splits,
       pl.gh_kps, pl.win_tt, pl.tt_fastest, (int64_t)pl.fwd_bytes, (int64_t)pl.bwd_bytes,
-      (int64_t)pl.bytes, p->n_tokens * pl.vc * 2, pl.fwd_tile_v, pl.dz_tile_v};
+      (int64_t)pl.bytes, p->n_tokens * pl.vc * 2, pl.fwd_tile_v, pl.dz_tile_v,
+      pl.gemm_tile_n};
   const int k = n_out < FLCE_PLAN_FIELDS ? n_out : FLCE_PLAN_FIELDS;
   for (int i = 0; i < k; ++i) out[i] = v[i];
   return k;
@@ -717,8 +721,9 @@ int flce_backward(const flce_problem* p, const void* hidden, const void* weight,
   g.hdim = (int)h;
   g.gh_splits = pl.gh_splits;
   g.gh_kps = (int)pl.gh_kps;
+  g.tile_n = pl.gemm_tile_n;
   g.gh_m_tiles = (int)cdiv(n, kGemmTileM);
-  g.n_tiles = (int)cdiv(h, kGemmTileN);
+  g.n_tiles = (int)cdiv(h, pl.gemm_tile_n);
   g.gh = slots ? ghpart : grad_hidden;
   g.n_dev = rows.n_dev;
 

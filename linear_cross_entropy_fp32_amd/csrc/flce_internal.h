@@ -22,9 +22,16 @@ constexpr int kLogitTileN = 256;
 constexpr int kNarrowTileV = 128;
 constexpr int kWideTileV = 256;
 constexpr int kFwdWideMinHidden = 1024;
-// Contraction tiles (grad_hidden, grad_weight): 256 x 128 outputs.
+// Contraction tiles (grad_hidden, grad_weight): 256 output rows and either
+// 128 columns (four waves in a 2 x 2 grid, a three-stage ring, two workgroups
+// per CU) or 256 columns (eight waves in a 2 x 4 grid, a four-stage ring, one
+// workgroup per CU); every wave owns 128 x 64 outputs.  The wide shape is
+// taken when H is a multiple of 256 from kContractWideMinHidden on (at
+// H = 640 a third of its last column tile would be padding).
 constexpr int kGemmTileM = 256;
-constexpr int kGemmTileN = 128;
+constexpr int kGemmTileNNarrow = 128;
+constexpr int kGemmTileNWide = 256;
+constexpr int kContractWideMinHidden = 1024;
 constexpr int kSliceK = 32;   // K values per pipeline slice
 constexpr int kFinalTokens = 8;   // tokens per block of the forward merge
 
@@ -117,6 +124,7 @@ struct ContractArgs {
   const uint16_t* w;     // lm_head rows of the chunk: w + c0 * H
   const uint16_t* h;     // [N, H] bf16 (fp32 hidden rounded to bf16)
   int n, hdim, width;    // tokens, hidden, vocab rows in the chunk
+  int tile_n;            // output columns per tile: kGemmTileNNarrow or kGemmTileNWide
   int gh_splits, gh_kps, gh_m_tiles, n_tiles;
   int gw_m_tiles, gw_rows_per_unit;   // unit u: gh split u, then gw tile rows of the unit
   float* gh;             // [gh_splits, N, H] partials, or grad_hidden when gh_splits == 1

@@ -32,8 +32,11 @@ static_assert(kSliceK == kBK, "slice depth");
 // waves on every SIMD (8 waves per CU).
 using NarrowTile = Tile<kNarrowTileV, kLogitTileN, true, true, 2, 2, 3>;
 using WideTile = Tile<kWideTileV, kLogitTileN, true, true, 4, 2, 4>;
-using GhTile = Tile<kGemmTileM, kGemmTileN, true, false>;          // dz . W
-using GwTile = Tile<kGemmTileM, kGemmTileN, false, false>;         // dz^T . h
+// contraction tiles (see kGemmTileNNarrow / kGemmTileNWide)
+using GhTile = Tile<kGemmTileM, kGemmTileNNarrow, true, false>;                  // dz . W
+using GwTile = Tile<kGemmTileM, kGemmTileNNarrow, false, false>;                 // dz^T . h
+using GhTileWide = Tile<kGemmTileM, kGemmTileNWide, true, false, 2, 4, 4>;
+using GwTileWide = Tile<kGemmTileM, kGemmTileNWide, false, false, 2, 4, 4>;
 constexpr int kColumns = NarrowTile::TN;     // token columns per lane
 constexpr int kQ = NarrowTile::TM * 16;      // values per token column per lane
 constexpr int kWaveRows = 64;                // vocabulary rows per wave
@@ -862,18 +865,18 @@ __device__ __forceinline__ void store_tile(const T& tile, float* c, int64_t ldc,
   // stores carry the non-temporal hint, which leaves fewer dirty L2 lines to
   // write back when the kernel ends.
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave & 1, wn = wave >> 1;
+  const int wm = wave % T::kWM, wn = wave / T::kWM;
   const __amdgpu_buffer_rsrc_t rs =
       tile_rsrc(c + (int64_t)m0 * ldc, (int64_t)(m_bound - m0) * ldc * 4);
 #pragma unroll
   for (int i = 0; i < T::TM; ++i)
 #pragma unroll
     for (int j = 0; j < T::TN; ++j) {
-      const int n = n0 + wn * (T::kBN / 2) + j * 32 + (lane & 31);
+      const int n = n0 + wn * (T::kBN / T::kWN) + j * 32 + (lane & 31);
       uint32_t off[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int m = wm * (T::kBM / 2) + i * 32 + acc_row(r, lane);
+        const int m = wm * (T::kBM / T::kWM) + i * 32 + acc_row(r, lane);
         off[r] = n < n_bound ? (uint32_t)(m * ldc + n) * 4 : kOutOfRange;
       }
       float v[16];
@@ -898,12 +901,12 @@ __device__ __forceinline__ void store_tile(const T& tile, float* c, int64_t ldc,
     }
 }
 
-constexpr int kContractLds =
-    GhTile::kLdsBytes > GwTile::kLdsBytes ? GhTile::kLdsBytes : GwTile::kLdsBytes;
-
-__global__ void __launch_bounds__(kThreads, 2)
+template <class GH, class GW>
+__global__ void __launch_bounds__(GH::kThr, wgs_per_cu<GH>())
 contract_kernel(const ContractArgs a) {
-  __shared__ __attribute__((aligned(16))) char lds[kContractLds];
+  static_assert(GH::kBM == GW::kBM && GH::kBN == GW::kBN && GH::kThr == GW::kThr, "tile pair");
+  __shared__ __attribute__((aligned(16))) char
+      lds[GH::kLdsBytes > GW::kLdsBytes ? GH::kLdsBytes : GW::kLdsBytes];
   const int width8 = (a.width + 7) & ~7;
   // The grid is cut into units, one per grad_hidden split: the split's tiles
   // (which share its dz columns and lm_head rows) followed by a run of
@@ -918,26 +921,26 @@ contract_kernel(const ContractArgs a) {
   if (off < gh_per_unit) {
     const int z = unit, rem = off;
     const int tm = rem / a.n_tiles, tn = rem % a.n_tiles;
-    if (tm * kGemmTileM >= n_rows) return;
+    if (tm * GH::kBM >= n_rows) return;
     const int kb = z * a.gh_kps;
     const int ke = min(a.width, kb + a.gh_kps);
-    const Operand opA{a.dz, a.ldz, tm * kGemmTileM, n_rows, width8};
-    const Operand opB{a.w, a.hdim, tn * kGemmTileN, a.hdim, a.width};
-    GhTile T;
+    const Operand opA{a.dz, a.ldz, tm * GH::kBM, n_rows, width8};
+    const Operand opB{a.w, a.hdim, tn * GH::kBN, a.hdim, a.width};
+    GH T;
     T.zero();
     T.run(lds, opA, opB, kb, ke);
-    store_tile(T, a.gh + (int64_t)z * a.n * a.hdim, a.hdim, tm * kGemmTileM, tn * kGemmTileN,
-               n_rows, a.hdim, a.gh_accumulate != 0);
+    store_tile(T, a.gh + (int64_t)z * a.n * a.hdim, a.hdim, tm * GH::kBM, tn * GH::kBN, n_rows,
+               a.hdim, a.gh_accumulate != 0);
   } else {
     const int b = off - gh_per_unit;
     const int tm = unit * a.gw_rows_per_unit + b / a.n_tiles, tn = b % a.n_tiles;
     if (tm >= a.gw_m_tiles) return;
-    const Operand opA{a.dz, a.ldz, tm * kGemmTileM, width8, n_rows};
-    const Operand opB{a.h, a.hdim, tn * kGemmTileN, a.hdim, n_rows};
-    GwTile T;
+    const Operand opA{a.dz, a.ldz, tm * GW::kBM, width8, n_rows};
+    const Operand opB{a.h, a.hdim, tn * GW::kBN, a.hdim, n_rows};
+    GW T;
     T.zero();
     T.run(lds, opA, opB, 0, n_rows);
-    store_tile(T, a.gw, a.hdim, tm * kGemmTileM, tn * kGemmTileN, a.width, a.hdim, false, true);
+    store_tile(T, a.gw, a.hdim, tm * GW::kBM, tn * GW::kBN, a.width, a.hdim, false, true);
   }
 }
 
@@ -1097,7 +1100,12 @@ hipError_t launch_contract(const ContractArgs& a, hipStream_t s) {
   const unsigned grid = (unsigned)(a.gh_splits *
                                    (a.gh_m_tiles * a.n_tiles + a.gw_rows_per_unit * a.n_tiles));
   if (grid == 0) return hipSuccess;
-  contract_kernel<<<grid, kThreads, 0, s>>>(a);
+  if (a.tile_n == kGemmTileNWide)
+    contract_kernel<GhTileWide, GwTileWide><<<grid, GhTileWide::kThr, 0, s>>>(a);
+  else if (a.tile_n == kGemmTileNNarrow)
+    contract_kernel<GhTile, GwTile><<<grid, GhTile::kThr, 0, s>>>(a);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

@@ -1,17 +1,18 @@
 // Tile engine for the fused linear cross-entropy kernels (gfx950 / CDNA4).
 //
-// A workgroup of 256 threads (4 waves of 64, a 2 x 2 wave grid) accumulates a
-// BM x BN fp32 tile of sum_k A(m, k) B(n, k) with bf16 MFMA
-// (v_mfma_f32_32x32x16_bf16); each wave owns TM x TN blocks of 32 x 32
-// (TM = BM/64, TN = BN/64).
+// A workgroup of WM x WN waves of 64 accumulates a BM x BN fp32 tile of
+// sum_k A(m, k) B(n, k) with bf16 MFMA (v_mfma_f32_32x32x16_bf16); each wave
+// owns TM x TN blocks of 32 x 32 (TM = BM / WM / 32, TN = BN / WN / 32).  The
+// kernels use 2 x 2 waves at two workgroups per CU and 4 x 2 or 2 x 4 waves
+// at one, so that every SIMD holds two waves either way.
 //
-// Operands stream HBM -> LDS in K slices of 32 values through a ring of three
-// LDS stages that buffer loads write directly (buffer_load_dwordx4 ... lds,
-// "LDS DMA"): no staging registers and no LDS store instructions.  Two slices
-// are in flight while one is multiplied, and a slice is consumed after an
-// explicit "s_waitcnt vmcnt(loads of one slice)" + s_barrier, so only that
-// slice has to have landed (a fenced barrier would make the compiler drain
-// every outstanding load).  Loads return in order, so the wait also holds
+// Operands stream HBM -> LDS in K slices of 32 values through a ring of
+// STAGES LDS stages that buffer loads write directly (buffer_load_dwordx4 ...
+// lds, "LDS DMA"): no staging registers and no LDS store instructions.
+// STAGES - 1 slices are in flight while one is multiplied, and a slice is
+// consumed after an explicit "s_waitcnt vmcnt(loads of the later slices)" +
+// s_barrier, so only that slice has to have landed (a fenced barrier would
+// make the compiler drain every outstanding load).  Loads return in order, so the wait also holds
 // when the caller's epilogue has issued other memory operations in between.
 // The streamed loop (run_stream) barriers at the start of each slice; the
 // single-tile loop (run) barriers in the middle of each slice, so that the
@@ -52,9 +53,8 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 
-constexpr int kThreads = 256;
 constexpr int kBK = 32;        // K values per slice
-constexpr int kStages = 3;     // LDS ring depth
+constexpr int kStages = 3;     // LDS ring depth of the four-wave tiles
 // Wave priority (s_setprio) while a tile's K loop runs; epilogues and result
 // stores run at 0.  With two workgroups per CU, a SIMD holds one wave of
 // each: when one is in its VALU-heavy epilogue and the other in its K loop,
@@ -173,24 +173,19 @@ __device__ __forceinline__ uint32_t lds_addr(const char* p) {
 
 // Wait until at most N of this wave's vector memory operations are
 // outstanding, then barrier the workgroup.
+#define FLCE_VMB(n) \
+  else if constexpr (N == n) asm volatile("s_waitcnt vmcnt(" #n ") lgkmcnt(0)\n\ts_barrier" ::: "memory");
 template <int N>
 __device__ __forceinline__ void vm_barrier() {
-  static_assert(N >= 0 && N <= 12, "vmcnt immediate");
+  static_assert(N >= 0 && N <= 24, "vmcnt immediate");
   // lgkmcnt(0): this wave's LDS reads of the stage about to be refilled are done
   if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  else if constexpr (N == 1) asm volatile("s_waitcnt vmcnt(1) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  else if constexpr (N == 2) asm volatile("s_waitcnt vmcnt(2) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  else if constexpr (N == 3) asm volatile("s_waitcnt vmcnt(3) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  else if constexpr (N == 4) asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  else if constexpr (N == 5) asm volatile("s_waitcnt vmcnt(5) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  else if constexpr (N == 6) asm volatile("s_waitcnt vmcnt(6) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  else if constexpr (N == 7) asm volatile("s_waitcnt vmcnt(7) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  else if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  else if constexpr (N == 9) asm volatile("s_waitcnt vmcnt(9) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  else if constexpr (N == 10) asm volatile("s_waitcnt vmcnt(10) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  else if constexpr (N == 11) asm volatile("s_waitcnt vmcnt(11) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  else asm volatile("s_waitcnt vmcnt(12) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  FLCE_VMB(1) FLCE_VMB(2) FLCE_VMB(3) FLCE_VMB(4) FLCE_VMB(5) FLCE_VMB(6) FLCE_VMB(7) FLCE_VMB(8)
+  FLCE_VMB(9) FLCE_VMB(10) FLCE_VMB(11) FLCE_VMB(12) FLCE_VMB(13) FLCE_VMB(14) FLCE_VMB(15)
+  FLCE_VMB(16) FLCE_VMB(17) FLCE_VMB(18) FLCE_VMB(19) FLCE_VMB(20) FLCE_VMB(21) FLCE_VMB(22)
+  FLCE_VMB(23) FLCE_VMB(24)
 }
+#undef FLCE_VMB
 
 // s_waitcnt lgkmcnt(0) in a form the compiler sees (vmcnt and expcnt left at
 // their maxima), so that it knows the LDS reads issued so far have completed
@@ -437,18 +432,18 @@ struct Tile {
   // k_begin must be a multiple of 32 unless k_end is the operands' K bound
   // (past which loads read zero).
   //
-  // Schedule.  Slice kt lives in stage kt % 3.  The workgroup barrier sits in
-  // the middle of each slice: after the MFMAs of its first K step, a wave
-  // waits until slice kt+1 has landed (loads of one slice may stay in
-  // flight) and until every wave has read slice kt, then refills stage kt % 3
-  // with slice kt+3, reads the first fragments of slice kt+1, and multiplies
-  // the second K step of slice kt meanwhile.  So the LDS reads after a
-  // barrier overlap MFMAs of the same wave, and two slices stay in flight.
+  // Schedule.  Slice kt lives in stage kt % S (S = STAGES).  The workgroup
+  // barrier sits in the middle of each slice: after the MFMAs of its first K
+  // step, a wave waits until slice kt+1 has landed (the loads of S - 2 later
+  // slices may stay in flight) and until every wave has read slice kt, then
+  // refills stage kt % S with slice kt+S, reads the first fragments of slice
+  // kt+1, and multiplies the second K step of slice kt meanwhile.  So the LDS
+  // reads after a barrier overlap MFMAs of the same wave, and S - 1 slices
+  // stay in flight.
   // Loads past the last slice are issued as zero-reading loads, which keeps
   // the wait counts the same in every iteration.
   __device__ __forceinline__ void run(char* lds, const Operand a_op, const Operand b_op,
                                       int k_begin, int k_end) {
-    static_assert(STAGES == 3, "the single-tile loop keeps three slices in flight");
     const int kt_total = (k_end - k_begin + kBK - 1) / kBK;
     if (kt_total <= 0) return;
     const typename SA::Plan a = SA::plan(a_op);
@@ -461,24 +456,23 @@ struct Tile {
       SA::issue(a, m0, k0, live);
       SB::issue(b, m0 + kLdsA, k0, live);
     };
-    issue(0, 0);
-    issue(1, 1);
-    issue(2, 2);
+#pragma unroll
+    for (int i = 0; i < STAGES; ++i) issue(i, i);
     bf16x8 fa0[TM], fb0[TN], fa1[TM], fb1[TN];
     __builtin_amdgcn_s_setprio(kLoopPriority);
-    vm_barrier<2 * kLoads>();            // slice 0 landed
+    vm_barrier<(STAGES - 1) * kLoads>();  // slice 0 landed
     frags(lds, 0, fa0, fb0);
     int st = 0;                           // stage of slice kt
     for (int kt = 0; kt < kt_total; ++kt) {
-      const int nst = st == kStages - 1 ? 0 : st + 1;
+      const int nst = st == STAGES - 1 ? 0 : st + 1;
       frags(lds + st * kStage, 1, fa1, fb1);
       mma(fa0, fb0);
       // keep the compiler from moving these MFMAs past the barrier, where the
       // wait for the reads above would then stand alone
       __builtin_amdgcn_sched_barrier(0);
       lds_reads_done();
-      vm_barrier<kLoads>();              // slice kt+1 landed; slice kt read by every wave
-      issue(kt + 3, st);
+      vm_barrier<(STAGES - 2) * kLoads>();  // slice kt+1 landed; slice kt read by every wave
+      issue(kt + STAGES, st);
       if (kt + 1 < kt_total) frags(lds + nst * kStage, 0, fa0, fb0);
       mma(fa1, fb1);
       st = nst;

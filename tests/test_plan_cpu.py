@@ -56,6 +56,7 @@ def test_offsets_stay_in_32_bits(chunk):
         dt = pl["dz_tile_rows"]
         assert dt == (256 if n * 2 * 256 < U31 else 128), label
         assert pl["fwd_tile_rows"] == (256 if h >= 1024 else 128), label
+        assert pl["contract_tile_cols"] == (256 if h >= 1024 and h % 256 == 0 else 128), label
         assert vc % dt == 0 and vc >= dt, label
         assert pl["n_chunks"] == -(-v // vc), label
         width = min(vc, v)
