@@ -113,23 +113,17 @@ __device__ __forceinline__ u32x4 dma_rsrc(const void* base, int64_t bytes) {
 }
 
 // 16 bytes per lane from global memory into LDS: lane l of the wave writes
-// bytes [16 l, 16 l + 16) of the 1 KB block at `lds` (wave-uniform); offsets
-// at or past the descriptor size read zero.  Issued as inline assembly so that
-// the compiler does not track the LDS writes: it would otherwise wait for
-// every outstanding load before each transposing LDS read.  Completion is
-// ordered by vm_barrier() alone; the waits the compiler places for its own
-// loads stay sufficient, since loads return in order and these only add to
-// the count.  Being volatile, the statement keeps its place between the
-// barriers.  The s_nop covers the one wait state that GFX9 needs between an
-// M0 write and an LDS-DMA instruction.
-__device__ __forceinline__ void dma16(const u32x4& rs, const char* lds, uint32_t off) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane(
-      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)lds);
-  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(off), "s"(rs),
-               "{m0}"(m0));
-}
-
-// Same, with the LDS byte address of the 1 KB block given (wave-uniform).
+// bytes [16 l, 16 l + 16) of the 1 KB block at LDS byte address m0
+// (wave-uniform); offsets at or past the descriptor size read zero.  Issued
+// as inline assembly so that the compiler does not track the LDS writes: it
+// would otherwise wait for every outstanding load before each transposing
+// LDS read.  Completion is ordered by vm_barrier() alone; the waits the
+// compiler places for its own loads stay sufficient, since loads return in
+// order and these only add to the count.  Being volatile, the statement keeps
+// its place between the barriers.  The s_nop covers the one wait state that
+// GFX9 needs between an M0 write and an LDS-DMA instruction.  Callers form m0
+// from the workgroup's LDS base (lds_addr) with scalar adds, so that no
+// address conversion runs per load.
 __device__ __forceinline__ void dma16_at(const u32x4& rs, uint32_t m0, uint32_t off) {
   asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(off), "s"(rs),
                "{m0}"(m0));
@@ -224,15 +218,17 @@ struct Stage<R, true, NW> {
     return Src{dma_rsrc(op.ptr + (int64_t)op.row0 * op.ld, rows * op.ld * 2),
                (uint32_t)(op.ld * 2), op.k_bound};
   }
-  __device__ static __forceinline__ void issue(const Src& s, char* lds, int k0) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // m0: LDS byte address of the stage's operand block (wave-uniform)
+  __device__ static __forceinline__ void issue(const Src& s, uint32_t m0, int k0) {
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 #pragma unroll
     for (int i = 0; i < kPerWave; ++i) {
       const int blk = wave * kPerWave + i;          // 1 KB block = 16 rows
       const int p = blk * 64 + lane;                // 16-byte slot this lane writes
       const int row = p >> 2, c = (p & 3) ^ swz(row);
       const int gk = k0 + c * 8;
-      dma16(s.rsrc, lds + blk * 1024, offset_or_oob(gk < s.k_bound, row * s.ld_bytes + gk * 2));
+      dma16_at(s.rsrc, m0 + blk * 1024, offset_or_oob(gk < s.k_bound, row * s.ld_bytes + gk * 2));
     }
   }
   // Per-lane load offsets of one tile, computed once: slice k0 adds 2 k0
@@ -296,15 +292,17 @@ struct Stage<R, false, NW> {
     return Src{dma_rsrc(op.ptr + op.row0, ((int64_t)op.k_bound * op.ld - op.row0) * 2),
                (uint32_t)(op.ld * 2), op.row_bound - op.row0};
   }
-  __device__ static __forceinline__ void issue(const Src& s, char* lds, int k0) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // m0: LDS byte address of the stage's operand block (wave-uniform)
+  __device__ static __forceinline__ void issue(const Src& s, uint32_t m0, int k0) {
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 #pragma unroll
     for (int i = 0; i < kPerWave; ++i) {
       const int blk = wave * kPerWave + i;
       const int p = blk * 64 + lane;
       const int k = p / kCPR, c = (p % kCPR) ^ swz(k);
-      dma16(s.rsrc, lds + blk * 1024,
-            offset_or_oob(c * 8 < s.rows, (uint32_t)(k0 + k) * s.ld_bytes + c * 16));
+      dma16_at(s.rsrc, m0 + blk * 1024,
+               offset_or_oob(c * 8 < s.rows, (uint32_t)(k0 + k) * s.ld_bytes + c * 16));
     }
   }
   // Per-lane load offsets of one tile, computed once: slice k0 adds k0 K
@@ -502,9 +500,10 @@ struct Tile {
     int it = 0, is = 0, islot = 0, ibuf = 0;
     Operand ao = a_op;
     typename SA::Src a = SA::source(ao);
+    const uint32_t l0 = lds_addr(lds);
     auto issue_next = [&]() {
       const int k0 = (it < ntiles ? is : past) * kBK;
-      char* buf = lds + islot * kStage;
+      const uint32_t buf = l0 + islot * kStage;
       if constexpr (ROWS) {
         if (is == 0 && it < ntiles) {
           const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
