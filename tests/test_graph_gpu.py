@@ -30,7 +30,9 @@ def _step(h, wt, t, b, go, w, ws):
 
 @pytest.mark.parametrize("w", [synth.small_workload(500, 192, 5000, 61, softcap=30.0, bias=True,
                                                     reduction="none"),
-                               synth.small_workload(256, 256, 32000, 62, reduction="none")],
+                               synth.small_workload(256, 256, 32000, 62, reduction="none"),
+                               synth.small_workload(600, 1024, 3000, 63, bias=True,
+                                                    reduction="none")],
                          ids=lambda w: w.name)
 def test_graph_replays_match_eager(w):
     dev = "cuda:0"

@@ -62,6 +62,11 @@ SMALL = [
     # H = 1024, where the forward takes 256-row tiles; running-max softcap path
     synth.small_workload(700, 1024, 5000, 43, softcap=50.0, logit_scale=2.0, bias=True,
                          reduction="none"),
+    # H = 1152: 256-row forward and dz tiles with the 256x128 contraction; ragged N and V
+    synth.small_workload(520, 1152, 4100, 44, softcap=30.0, bias=True, reduction="none"),
+    # H = 2048 with both operands fp32: the 256x256 contraction on the rounded copies
+    synth.small_workload(300, 2048, 2600, 45, hidden_dtype="f32", weight_dtype="f32",
+                         targets="zipf", reduction="sum"),
 ]
 
 
