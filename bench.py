@@ -276,6 +276,9 @@ def write_traffic_record(args) -> int:
 
 PER_CONFIG = ("tiny", "huge_vocab", "bias_none", "zipf_sum", "fp32_hidden",
               "fp32_hidden_all_ignored")
+# workloads also timed as a graph-replayed step: tiny is launch-bound, and
+# huge_vocab shows what a graph saves on the headline step
+GRAPH_CONFIGS = ("tiny", "huge_vocab")
 WARMUP_MS = 25.0
 FLUSH_BYTES = 512 << 20
 
@@ -435,6 +438,44 @@ def pct(xs, q):
     return float(np.percentile(xs, q))
 
 
+def graph_steps(r: Runner, hip, steps: int) -> list:
+    """The same step captured once in a HIP graph (the library allocates
+    nothing and issues no memset, so both calls capture as plain launches)
+    and replayed: per-step times with the flushed protocol, in ms.  For a
+    launch-bound workload the difference to the eager step is the launch
+    cost."""
+    import torch
+    cs = torch.cuda.Stream()
+    old = r.sp
+    r.sp = ctypes.c_void_p(cs.cuda_stream)
+    cs.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cs):
+        r.fwd()
+        r.bwd()
+    cs.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=cs):
+        r.fwd()
+        r.bwd()
+    r.sp = old
+    sp = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda:0")
+    ev = Events(hip, 2 * steps)
+    for i in range(steps + 2):            # two untimed replays
+        flush.fill_(i & 255)
+        k = i - 2
+        if k >= 0:
+            _hip_ok(hip.hipEventRecord(ctypes.c_void_p(ev[2 * k]), sp))
+        g.replay()
+        if k >= 0:
+            _hip_ok(hip.hipEventRecord(ctypes.c_void_p(ev[2 * k + 1]), sp))
+    torch.cuda.synchronize()
+    out = [ev.ms(2 * k, 2 * k + 1) for k in range(steps)]
+    ev.close()
+    del g, flush
+    return out
+
+
 def per_config(args, hip) -> dict:
     """Every workload of the metric, fewer steps each: ms/step (median of the
     flushed steps), tokens/s, TFLOP/s and % of the bf16 peak (8NHV), the
@@ -461,6 +502,10 @@ def per_config(args, hip) -> dict:
                "pct_bf16_peak": 100.0 * flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
                "fwd_ms": pct(m["fwd"], 50), "bwd_ms": pct(m["bwd"], 50),
                "n_valid": int(r.red_i[0].item())}
+        if name in GRAPH_CONFIGS:
+            gm = pct(graph_steps(r, hip, max(3, args.per_config_steps)), 50)
+            rec["graph_ms_per_step"] = gm
+            rec["graph_tokens_per_s"] = w.n_tokens / (gm * 1e-3)
         if not args.no_cpu_baseline and w.targets != "all_ignored":
             cb = cpu_baseline(w, r.inp, args.per_config_cpu_seconds)
             rec["cpu_oracle_tokens_per_s"] = cb["value"]
