@@ -150,8 +150,8 @@ int flce_forward(const flce_problem* p, const void* hidden, const void* weight,
  * library holds in device memory, 16 MiB per GPU, from the first call on that
  * GPU until the process ends (the device is the one `stream` belongs to).
  * Nothing is allocated: a problem whose forward needs more than 16 MiB of
- * scratch (flce_plan_info field 9: e.g. fp32 hidden states, whose bf16 split
- * alone is 4*N*H bytes) returns FLCE_ERR_WORKSPACE before anything is
+ * scratch (flce_plan_info field 9: e.g. fp32 hidden states, whose bf16 copy
+ * alone is 2*N*H bytes) returns FLCE_ERR_WORKSPACE before anything is
  * launched.  Every call on one GPU shares that GPU's array: calls that
  * overlap on one GPU (other streams, other threads) race, so serialise them.
  * The first call on a device also looks the array's address up (no

@@ -85,11 +85,11 @@ struct Plan {
   int win_tt;            // token tiles per window of the logit-tile order
   int tt_fastest;        // logit-tile workgroup order: token tile fastest when
                          // the bf16 hidden operand fits in one XCD's L2
-  size_t off_hsplit, off_part, off_bsums, off_dz, off_ghpart, off_cspart;
+  size_t off_hbf16, off_part, off_bsums, off_dz, off_ghpart, off_cspart;
   // row compaction: perm [N] int32, cnt [2] int32, block scratch, compact
-  // bf16 hidden rows [N, H] (fp32 hidden: the hi / lo split rows instead)
+  // bf16 hidden rows [N, H] (fp32 hidden: its bf16 copy holds the compact rows)
   size_t off_perm, off_cnt, off_blk, off_hc;
-  size_t off_wsplit;     // fp32 lm_head: rounded to bf16 [V, H]
+  size_t off_wbf16;      // fp32 lm_head: rounded to bf16 [V, H]
   size_t off_zt;         // fp32 operand: the exact target logits [N] (forward part)
   size_t fwd_bytes, bwd_bytes, bytes;
 };
@@ -205,9 +205,9 @@ Plan make_plan(const flce_problem* p) {
   pl.gh_splits = (int)cdiv(width, pl.gh_kps);
 
   size_t off = 0;
-  pl.off_wsplit = off;
+  pl.off_wbf16 = off;
   if (p->weight_dtype == FLCE_F32) off += aup(size_t(v) * h * 2);
-  pl.off_hsplit = off;
+  pl.off_hbf16 = off;
   if (p->hidden_dtype == FLCE_F32) off += aup(size_t(n) * h * 2);
   pl.off_perm = pl.off_cnt = pl.off_blk = pl.off_hc = off;
   if (p->compact_valid && n > 0) {
@@ -309,7 +309,7 @@ int prepare_rows(const flce_problem* p, const Plan& pl, const void* hidden, cons
   r = Rows{};
   r.w0 = static_cast<const uint16_t*>(weight);
   if (p->weight_dtype == FLCE_F32) {
-    uint16_t* wb = reinterpret_cast<uint16_t*>(ws + pl.off_wsplit);
+    uint16_t* wb = reinterpret_cast<uint16_t*>(ws + pl.off_wbf16);
     if (launch && (rc = hip_check(launch_round_bf16(static_cast<const float*>(weight), wb,
                                                     p->vocab * h, s),
                                   "round_weight")))
@@ -318,7 +318,7 @@ int prepare_rows(const flce_problem* p, const Plan& pl, const void* hidden, cons
   }
   r.h0 = static_cast<const uint16_t*>(hidden);
   if (n == 0) return FLCE_OK;
-  uint16_t* hb = reinterpret_cast<uint16_t*>(ws + pl.off_hsplit);
+  uint16_t* hb = reinterpret_cast<uint16_t*>(ws + pl.off_hbf16);
   if (p->compact_valid) {
     int* perm = reinterpret_cast<int*>(ws + pl.off_perm);
     int* cnt = reinterpret_cast<int*>(ws + pl.off_cnt);

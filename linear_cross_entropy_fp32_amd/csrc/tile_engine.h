@@ -144,11 +144,12 @@ __device__ __forceinline__ void dma4_at(const u32x4& rs, uint32_t m0, uint32_t o
 
 // Per-row values of the A operand (an fp32 bias) for the epilogues of a
 // streamed tile sequence (Tile::run_stream with ROWS): each wave loads the 64
-// values of its half of a tile's 128 A rows (wave w: rows 64 (w % 2) + lane)
-// by LDS DMA together with the tile's first slice, into its own 256-byte
-// block of buffer t % 3.  Counted with that slice's loads, they have landed
+// values of its slab of a tile's A rows (wave w: rows 64 (w % WM) + lane) by
+// LDS DMA together with the tile's first slice, into its own 256-byte block
+// of buffer t % STAGES.  Counted with that slice's loads, they have landed
 // when the tile's last slice has, and the buffer is not loaded again before
-// the tile's epilogue is done (the issue pointer runs two slices ahead).
+// the tile's epilogue is done (the issue pointer runs STAGES - 1 slices
+// ahead).
 struct RowDma {
   u32x4 rsrc;      // 4-byte values per A row; rows past its size read zero
   uint32_t lds;    // LDS byte address of buffer 0 (row_dma_bytes(...))
