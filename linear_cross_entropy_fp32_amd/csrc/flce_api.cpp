@@ -37,7 +37,9 @@ constexpr int64_t kMaxElems = int64_t(1) << 31;      // V*H stays int32-indexabl
 constexpr int64_t kMaxOperandBytes = (int64_t(1) << 31) - 1;
 constexpr size_t kAlign = 256;
 constexpr int64_t kTargetWgs = 2048;                 // forward workgroups: ~8 per CU
-constexpr int64_t kDzWgs = 256;                      // dz workgroups per chunk: one round (one per CU)
+constexpr int64_t kCus = 256;
+constexpr int64_t kDzWgs = kCus;                     // dz workgroups per chunk and workgroup per CU:
+                                                     // one round
 // ... unless that would give a workgroup more vocab tiles than this (at N =
 // 16384 with 16384-row chunks: 8 tiles in two rounds measured 1% faster than
 // 16 in one)
@@ -159,19 +161,28 @@ Plan make_plan(const flce_problem* p) {
   // and at least N rows wide (so a grad_hidden tile's K, the chunk's rows,
   // is never shorter than a grad_weight tile's K, the N tokens), as long as
   // the chunk stays below the 2^31-byte operand limit
-  pl.dz_tile_v = n * 2 * kWideTileV <= kMaxOperandBytes ? kWideTileV : kNarrowTileV;
+  auto chunk_rows = [&](int64_t dt) {
+    int64_t vc = n > 0 ? (kDzChunkBytes / (2 * n)) / dt * dt : rup(v, dt);
+    if (n > 0 && vc < kMinChunkWidth)
+      vc = (kDzChunkBytesWide / (2 * n)) / dt * dt;
+    if (n > 0) {
+      vc = std::max<int64_t>(vc, rup(n, dt));
+      vc = std::min<int64_t>(vc, kMaxOperandBytes / (2 * n) / dt * dt);
+    }
+    vc = std::min<int64_t>(vc, kMaxOperandBytes / (2 * h) / dt * dt);
+    vc = std::min<int64_t>(vc, kMaxChunkRows);
+    vc = std::max<int64_t>(vc, dt);
+    return std::min<int64_t>(vc, rup(v, dt));
+  };
+  // dz tiles: 256 rows, unless one 256-row column of dz would pass the 2^31-byte
+  // descriptor extent, or a chunk holds fewer 256-row tiles than there are CUs
+  // (one workgroup per CU would leave CUs idle; 128-row tiles double the count)
+  pl.dz_tile_v = kWideTileV;
+  if (n * 2 * kWideTileV > kMaxOperandBytes ||
+      pl.n_tok_tiles * cdiv(chunk_rows(kWideTileV), kWideTileV) < kCus)
+    pl.dz_tile_v = kNarrowTileV;
   const int64_t dt = pl.dz_tile_v;
-  int64_t vc = n > 0 ? (kDzChunkBytes / (2 * n)) / dt * dt : rup(v, dt);
-  if (n > 0 && vc < kMinChunkWidth)
-    vc = (kDzChunkBytesWide / (2 * n)) / dt * dt;
-  if (n > 0) {
-    vc = std::max<int64_t>(vc, rup(n, dt));
-    vc = std::min<int64_t>(vc, kMaxOperandBytes / (2 * n) / dt * dt);
-  }
-  vc = std::min<int64_t>(vc, kMaxOperandBytes / (2 * h) / dt * dt);
-  vc = std::min<int64_t>(vc, kMaxChunkRows);
-  vc = std::max<int64_t>(vc, dt);
-  vc = std::min<int64_t>(vc, rup(v, dt));
+  const int64_t vc = chunk_rows(dt);
   pl.vc = vc;
   pl.n_chunks = (int)cdiv(v, vc);
   const int64_t chunk_tiles = vc / dt;
@@ -180,7 +191,9 @@ Plan make_plan(const flce_problem* p) {
   // which keeps the GPU filled when a third of the rows carry a loss
   pl.dz_tiles_per_wg = (int)std::max<int64_t>(
       1, std::min<int64_t>(kMaxDzTilesPerWg,
-                           chunk_tiles * pl.n_tok_tiles / kDzWgs / (p->compact_valid ? 2 : 1)));
+                           chunk_tiles * pl.n_tok_tiles /
+                               (kDzWgs * (pl.dz_tile_v == kWideTileV ? 1 : 2)) /
+                               (p->compact_valid ? 2 : 1)));
   // with a large hidden operand, fewer tiles per workgroup (more vocabulary
   // groups per window) until the token tiles an XCD holds at once keep their
   // hidden rows within half of its L2

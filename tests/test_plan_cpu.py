@@ -52,9 +52,17 @@ def test_offsets_stay_in_32_bits(chunk):
         pl = flce.flce_plan_info(p)
         vc = pl["chunk_rows"]
         label = (n, h, v, p.hidden_dtype, p.weight_dtype, p.compact_valid, vc)
-        # 256-row logit tiles, except where the operand or dz extent needs 128
+        # 256-row dz tiles, except where one 256-row dz column would pass the
+        # descriptor extent, or where a chunk holds fewer 256-row tiles than
+        # the 256 CUs
         dt = pl["dz_tile_rows"]
-        assert dt == (256 if n * 2 * 256 < U31 else 128), label
+        ntt = -(-n // 256)
+        if n * 2 * 256 >= U31:
+            assert dt == 128, label
+        elif dt == 256:
+            assert ntt * -(-min(vc, v) // 256) >= 256, label
+        else:
+            assert dt == 128 and ntt * -(-min(vc, v) // 256) < 256, label
         assert pl["fwd_tile_rows"] == (256 if h >= 1024 else 128), label
         assert pl["contract_tile_cols"] == (256 if h >= 1024 and h % 256 == 0 else 128), label
         assert vc % dt == 0 and vc >= dt, label
