@@ -75,11 +75,12 @@ def library_gemm(args) -> int:
     the loss path."""
     import torch
 
-    from linear_cross_entropy_fp32_amd import synth
+    from linear_cross_entropy_fp32_amd import _binding, synth
     w = synth.WORKLOADS[args.workload]
     n, hd, v = w.n_tokens, w.hidden, w.vocab
-    vc = max(128, ((1 << 27) // (2 * n)) // 128 * 128)     # the backward's chunk width
-    vc = min(vc, v)
+    prob = _binding.make_problem(n, hd, v, hidden_dtype=1 if w.hidden_dtype == "f32" else 0,
+                                 weight_dtype=1 if w.weight_dtype == "f32" else 0)
+    vc = min(int(_binding.flce_plan_info(prob)["chunk_rows"]), v)   # the backward's chunk width
     dev = torch.device("cuda:0")
     g = torch.Generator(device="cpu").manual_seed(0)
 
