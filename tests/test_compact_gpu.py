@@ -55,6 +55,8 @@ CASES = [
     synth.small_workload(260, 64, 900, 37, targets="all_ignored", hidden_dtype="f32"),
     synth.small_workload(800, 96, 2000, 42, weight_dtype="f32", hidden_dtype="f32",
                          prompt_frac=0.6, prompt_block=200, softcap=30.0),
+    # H = 640: 128-row dz tiles (one chunk of 25), two grad_hidden slots
+    synth.small_workload(900, 640, 3100, 45, softcap=30.0, bias=True, prompt_frac=0.6),
     # 256-row forward, dz and 256x256 contraction tiles (H a multiple of 256 from 1024 on)
     synth.small_workload(900, 1024, 3100, 43, softcap=30.0, bias=True, prompt_frac=0.6,
                          prompt_block=300, reduction="none"),

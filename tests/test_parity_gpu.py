@@ -67,6 +67,12 @@ SMALL = [
     # H = 2048 with both operands fp32: the 256x256 contraction on the rounded copies
     synth.small_workload(300, 2048, 2600, 45, hidden_dtype="f32", weight_dtype="f32",
                          targets="zipf", reduction="sum"),
+    # H = 640 (the 256 x 128 contraction, five column tiles): ragged N and V, three
+    # grad_hidden slots
+    synth.small_workload(300, 640, 2100, 46, softcap=30.0, bias=True),
+    synth.small_workload(2200, 640, 9000, 47, hidden_dtype="f32", reduction="none"),
+    # H = 640 over two vocabulary chunks, the last ragged
+    synth.small_workload(4100, 640, 20000, 48, softcap=30.0),
 ]
 
 
