@@ -695,8 +695,8 @@ def main() -> int:
     if args.traffic_record:
         return write_traffic_record(args)
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (got --gpus {args.gpus}); "
-              "the path's sharding is described in DESIGN.md", file=sys.stderr)
+        print(f"bench.py: the library runs on one GPU only (got --gpus {args.gpus}); "
+              "a multi-GPU split of the vocabulary or the tokens is not built", file=sys.stderr)
         return 2
     import torch
 
