@@ -63,7 +63,6 @@ constexpr int64_t kMinChunkWidth = 8192;
 // included), so 256 * 2 * Vc must stay well below 2^31 (here 2^30).  Only tiny
 // N reaches the cap: otherwise the 2^27..2^28-byte chunk rule is narrower.
 constexpr int64_t kMaxChunkRows = int64_t(1) << 21;
-constexpr int64_t kColsumElems = int64_t(1) << 22;   // fp32 partials of the grad_bias sums
 constexpr int64_t kL2Bytes = int64_t(4) << 20;        // L2 of one XCD
 // logit-tile workgroups one XCD (32 CUs) holds at once: two per CU of the
 // narrow tile, one of the wide
@@ -83,11 +82,11 @@ struct Plan {
   int dz_tiles_per_wg;   // vocab tiles streamed by one dz workgroup
   int gh_splits;         // split-K of the grad_hidden contraction
   int64_t gh_kps;
-  int cs_segs;           // row segments of the grad_bias column sums
+  int cs_rows;           // grad_bias partial rows (kColsumRowsPerTile per token tile)
   int win_tt;            // token tiles per window of the logit-tile order
   int tt_fastest;        // logit-tile workgroup order: token tile fastest when
                          // the bf16 hidden operand fits in one XCD's L2
-  size_t off_hbf16, off_part, off_bsums, off_dz, off_ghpart, off_cspart;
+  size_t off_hbf16, off_part, off_bsums, off_dz, off_ghpart, off_cspart, off_cstmp;
   // row compaction: perm [N] int32, cnt [2] int32, block scratch, compact
   // bf16 hidden rows [N, H] (fp32 hidden: its bf16 copy holds the compact rows)
   size_t off_perm, off_cnt, off_blk, off_hc;
@@ -248,9 +247,13 @@ Plan make_plan(const flce_problem* p) {
   // the split-K slots; with the row compaction also for one split, since the
   // final pass scatters the compact rows back
   if (pl.gh_splits > 1 || p->compact_valid) off += aup(size_t(pl.gh_splits) * n * h * 4);
-  pl.cs_segs = (int)std::max<int64_t>(1, std::min<int64_t>(cdiv(n, 256), kColsumElems / vc));
+  // grad_bias: partial rows of the dz epilogue, and with more than
+  // kColsumGroupRows of them one row per group for the two-pass sum
+  pl.cs_rows = (int)(int64_t(pl.n_tok_tiles) * kColsumRowsPerTile);
   pl.off_cspart = off;
-  off += aup(size_t(pl.cs_segs) * vc * 4);
+  off += aup(size_t(pl.cs_rows) * vc * 4);
+  pl.off_cstmp = off;
+  if (pl.cs_rows > kColsumGroupRows) off += aup(size_t(cdiv(pl.cs_rows, kColsumGroupRows)) * vc * 4);
   pl.bwd_bytes = off;
   pl.bytes = std::max(pl.fwd_bytes, pl.bwd_bytes);
   return pl;
@@ -723,6 +726,7 @@ int flce_backward(const flce_problem* p, const void* hidden, const void* weight,
   d.tiles_per_wg = pl.dz_tiles_per_wg;
   d.dz = dz;
   d.ldz = pl.vc;
+  d.cs_part = grad_bias ? reinterpret_cast<float*>(ws + pl.off_cspart) : nullptr;
   d.perm = rows.perm;
   d.n_dev = rows.n_dev;
 
@@ -762,9 +766,10 @@ int flce_backward(const flce_problem* p, const void* hidden, const void* weight,
       return rc;
 
     if (grad_bias &&
-        (rc = hip_check(launch_colsum(dz, pl.vc, (int)n, (int)width, pl.cs_segs,
-                                      reinterpret_cast<float*>(ws + pl.off_cspart),
-                                      grad_bias + c0, rows.n_dev, s),
+        (rc = hip_check(launch_colsum(reinterpret_cast<float*>(ws + pl.off_cspart), pl.vc,
+                                      pl.cs_rows, (int)n, rows.n_dev, kColsumRowsPerTile,
+                                      (int)width, reinterpret_cast<float*>(ws + pl.off_cstmp),
+                                      grad_bias + c0, s),
                         "colsum")))
       return rc;
   }

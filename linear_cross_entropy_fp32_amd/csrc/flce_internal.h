@@ -34,6 +34,9 @@ constexpr int kGemmTileNWide = 256;
 constexpr int kContractWideMinHidden = 1024;
 constexpr int kSliceK = 32;   // K values per pipeline slice
 constexpr int kFinalTokens = 8;   // tokens per block of the forward merge
+// grad_bias partial rows per 256-token tile (the dz tiles' wave columns)
+constexpr int kColsumRowsPerTile = 2;
+constexpr int kColsumGroupRows = 256;   // rows summed per group when there are more
 
 // Online softmax state of one token over a range of vocabulary rows, in base-2
 // units (u = z * log2 e): running max m, S = sum 2^(u-m), T = sum 2^(u-m) u,
@@ -110,6 +113,10 @@ struct DzArgs {
   int win_tt;            // token tiles per workgroup window (see grouped_order)
   uint16_t* dz;          // [N, ldz] bf16 chunk buffer
   int64_t ldz;
+  // grad_bias partials (null without grad_bias): row tt * kColsumRowsPerTile + wn
+  // holds the column sums of the stored dz over the 128 tokens of wave column
+  // wn of token tile tt, at the chunk's vocabulary offsets; stride ldz
+  float* cs_part;
   // row compaction (both null without it): dz row c belongs to row perm[c] of
   // tgt, lse and grad_out; only rows c < *n_dev are computed
   const int* perm;
@@ -165,8 +172,8 @@ hipError_t launch_sum_partials(const float* part, int nsplit, int64_t stride, fl
                                int64_t count, int64_t hdim, const int* perm, const int* n_dev,
                                hipStream_t s);
 // grad_bias of one chunk; part: nseg * width floats of workspace.
-hipError_t launch_colsum(const uint16_t* dz, int64_t ldz, int n_tok, int width, int nseg,
-                         float* part, float* out, const int* n_dev, hipStream_t s);
+hipError_t launch_colsum(const float* part, int64_t ld, int nseg, int n, const int* n_dev,
+                         int per_tile, int width, float* tmp, float* out, hipStream_t s);
 // Row compaction (see compact_scatter_kernel): perm [N], cnt [2] = {rows that
 // carry a loss, out-of-range targets}; blk: 2 * cdiv(N, 256) ints of scratch.
 // Then the hidden rows of the first cnt[0] compact rows are gathered into

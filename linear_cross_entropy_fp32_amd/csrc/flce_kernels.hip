@@ -723,6 +723,11 @@ struct DzEpilogue {
     constexpr int kRowLanes = kWaveRows * 2 / 16, kPassRows = 64 / kRowLanes;
     const uint32_t voff = (uint32_t)(lane / kRowLanes) * ld_bytes + (lane % kRowLanes) * 16 +
                           (vw - a.c0) * 2;
+    // grad_bias: this wave's column sums of the stored (bf16) dz over its 128
+    // tokens; lane l sums vocabulary rows 8 (l % 8) .. 8 (l % 8) + 7 of the slab
+    // over the token rows it stores
+    const bool cs = BIAS && a.cs_part != nullptr;
+    float csum[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < kColumns; ++j) {
       // the bias values are read again for every column, four at a time, so
@@ -796,6 +801,37 @@ struct DzEpilogue {
         // part of the range check)
         __builtin_amdgcn_raw_buffer_store_b128(x, out, voff + (j * 32 + pass * kPassRows) * ld_bytes,
                                                0, 0);
+        if constexpr (BIAS) {
+          if (cs) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              csum[2 * k] += __builtin_bit_cast(float, x[k] << 16);
+              csum[2 * k + 1] += __builtin_bit_cast(float, x[k] & 0xffff0000u);
+            }
+          }
+        }
+      }
+    }
+    if constexpr (BIAS) {
+      if (cs) {
+        // the kPassRows token rows of a pass sit in lanes l, l + 8, ...: a fixed
+        // butterfly over them, then lanes 0..7 hold the wave's sums
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          csum[e] += __shfl_xor(csum[e], 8);
+          csum[e] += __shfl_xor(csum[e], 16);
+          csum[e] += __shfl_xor(csum[e], 32);
+        }
+        static_assert(kRowLanes == 8 && kPassRows == 8, "column-sum lanes");
+        if (lane < kRowLanes) {
+          // one partial row per token tile and wave column: seg = nbase / 128
+          const int seg = nbase / (kLogitTileN / LT::kWN);
+          const int v = vw + 8 * lane;
+          float* dst = a.cs_part + (int64_t)seg * a.ldz + (v - a.c0);
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (v + e < a.v) dst[e] = csum[e];
+        }
       }
     }
   }
@@ -965,50 +1001,58 @@ __global__ void sum_partials_kernel(const float* __restrict__ part, int nsplit, 
   out[o] = s;
 }
 
-// grad_bias of one chunk, gb[v] = sum_n dz[n, v] (fp32 accumulation of the bf16
-// dz), in two fixed-order passes.  Pass 1: block (column block of 512, row
-// segment) has 64 column groups of 8 columns x 4 row phases; each thread
-// sums its rows with 16-byte loads, the 4 phases are added in order in LDS,
-// and the block writes part[seg][512 columns].  Pass 2 adds the segments in
-// order.
-constexpr int kColBlock = 512;
-__global__ void __launch_bounds__(256)
-colsum_partial_kernel(const uint16_t* __restrict__ dz, int64_t ldz, int n_tok, int width,
-                      int rows_per_seg, float* __restrict__ part, const int* __restrict__ n_dev) {
-  if (n_dev) n_tok = min(n_tok, *n_dev);
-  const int cg = threadIdx.x & 63, ph = threadIdx.x >> 6;
-  const int c0 = blockIdx.x * kColBlock + cg * 8;
-  const int seg = blockIdx.y;
-  const int r0 = seg * rows_per_seg, r1 = min(n_tok, r0 + rows_per_seg);
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  if (c0 < width) {
-    for (int n = r0 + ph; n < r1; n += 4) {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(dz + (int64_t)n * ldz + c0);
+// grad_bias of a chunk: out[v] = sum over the partial rows written by the dz
+// epilogue (one per token tile and wave column, in row order).  Rows of token
+// tiles past the computed rows (row compaction) were never written and are
+// not read.  More than kColsumGroup rows are summed in two fixed-order
+// passes: groups of kColsumGroup rows into tmp, then the groups.
+constexpr int kColsumGroup = kColsumGroupRows;
+static_assert(WideTile::kWN == kColsumRowsPerTile && NarrowTile::kWN == kColsumRowsPerTile,
+              "grad_bias partial rows per token tile");
+
+// s + rows [g0, g1) of column v, added in row order; the loads of 16 rows are
+// issued before their additions
+__device__ __forceinline__ float add_rows(float s, const float* __restrict__ p, int64_t ld, int v,
+                                          int g0, int g1) {
+  int g = g0;
+  for (; g + 16 <= g1; g += 16) {
+    float t[16];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        acc[2 * e] += __builtin_bit_cast(float, v[e] << 16);
-        acc[2 * e + 1] += __builtin_bit_cast(float, v[e] & 0xffff0000u);
-      }
-    }
-  }
-  __shared__ float red[4][kColBlock];
+    for (int k = 0; k < 16; ++k) t[k] = p[(int64_t)(g + k) * ld + v];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) red[ph][cg * 8 + e] = acc[e];
-  __syncthreads();
-  for (int c = threadIdx.x; c < kColBlock; c += 256) {
-    const int col = blockIdx.x * kColBlock + c;
-    if (col < width)
-      part[(int64_t)seg * width + col] = ((red[0][c] + red[1][c]) + red[2][c]) + red[3][c];
+    for (int k = 0; k < 16; ++k) s += t[k];
   }
+  for (; g < g1; ++g) s += p[(int64_t)g * ld + v];
+  return s;
 }
 
-__global__ void colsum_reduce_kernel(const float* __restrict__ part, int nseg, int width,
+__device__ __forceinline__ int colsum_rows(int nseg, int n, const int* n_dev, int per_tile) {
+  if (!n_dev) return nseg;
+  const int n_rows = min(n, *n_dev);
+  return min(nseg, (n_rows + kLogitTileN - 1) / kLogitTileN * per_tile);
+}
+
+__global__ void colsum_reduce_kernel(const float* __restrict__ part, int64_t ld, int nseg, int n,
+                                     const int* __restrict__ n_dev, int per_tile, int width,
+                                     float* __restrict__ tmp, float* __restrict__ out) {
+  const int v = blockIdx.x * blockDim.x + threadIdx.x;
+  if (v >= width) return;
+  const int rows = colsum_rows(nseg, n, n_dev, per_tile);
+  if (!tmp) {
+    out[v] = add_rows(0.f, part, ld, v, 0, rows);
+    return;
+  }
+  const int g0 = blockIdx.y * kColsumGroup, g1 = min(rows, g0 + kColsumGroup);
+  tmp[(int64_t)blockIdx.y * width + v] = add_rows(0.f, part, ld, v, g0, g1);
+}
+
+__global__ void colsum_groups_kernel(const float* __restrict__ tmp, int ngroups, int nseg, int n,
+                                     const int* __restrict__ n_dev, int per_tile, int width,
                                      float* __restrict__ out) {
   const int v = blockIdx.x * blockDim.x + threadIdx.x;
   if (v >= width) return;
-  float s = part[v];
-  for (int g = 1; g < nseg; ++g) s += part[(int64_t)g * width + v];
-  out[v] = s;
+  const int groups = (colsum_rows(nseg, n, n_dev, per_tile) + kColsumGroup - 1) / kColsumGroup;
+  out[v] = add_rows(0.f, tmp, width, v, 0, min(groups, ngroups));
 }
 
 __global__ void fill_zero_kernel(float* __restrict__ p, int64_t count) {
@@ -1118,15 +1162,20 @@ hipError_t launch_sum_partials(const float* part, int nsplit, int64_t stride, fl
   return hipGetLastError();
 }
 
-hipError_t launch_colsum(const uint16_t* dz, int64_t ldz, int n_tok, int width, int nseg,
-                         float* part, float* out, const int* n_dev, hipStream_t s) {
+hipError_t launch_colsum(const float* part, int64_t ld, int nseg, int n, const int* n_dev,
+                         int per_tile, int width, float* tmp, float* out, hipStream_t s) {
   if (width == 0) return hipSuccess;
-  if (n_tok == 0) return launch_fill_zero(out, width, s);
-  const int rows_per_seg = (n_tok + nseg - 1) / nseg;
-  nseg = (n_tok + rows_per_seg - 1) / rows_per_seg;
-  const dim3 grid((unsigned)((width + kColBlock - 1) / kColBlock), (unsigned)nseg);
-  colsum_partial_kernel<<<grid, 256, 0, s>>>(dz, ldz, n_tok, width, rows_per_seg, part, n_dev);
-  colsum_reduce_kernel<<<grid1(width, 256), 256, 0, s>>>(part, nseg, width, out);
+  // 64 columns per block: a chunk's few thousand columns reach many CUs
+  if (nseg <= kColsumGroup) {
+    colsum_reduce_kernel<<<grid1(width, 64), 64, 0, s>>>(part, ld, nseg, n, n_dev, per_tile,
+                                                         width, nullptr, out);
+    return hipGetLastError();
+  }
+  const int ngroups = (nseg + kColsumGroup - 1) / kColsumGroup;
+  const dim3 grid(grid1(width, 64), (unsigned)ngroups);
+  colsum_reduce_kernel<<<grid, 64, 0, s>>>(part, ld, nseg, n, n_dev, per_tile, width, tmp, out);
+  colsum_groups_kernel<<<grid1(width, 64), 64, 0, s>>>(tmp, ngroups, nseg, n, n_dev, per_tile,
+                                                       width, out);
   return hipGetLastError();
 }
 
