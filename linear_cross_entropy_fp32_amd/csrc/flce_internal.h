@@ -171,7 +171,10 @@ hipError_t launch_contract(const ContractArgs& a, hipStream_t s);
 hipError_t launch_sum_partials(const float* part, int nsplit, int64_t stride, float* out,
                                int64_t count, int64_t hdim, const int* perm, const int* n_dev,
                                hipStream_t s);
-// grad_bias of one chunk; part: nseg * width floats of workspace.
+// grad_bias of one chunk from the dz epilogue's partial rows: part holds nseg
+// rows (per_tile per token tile, stride ld; with row compaction only the rows
+// of the computed token tiles are read); tmp, one row of width floats per
+// kColsumGroupRows rows, is used when nseg exceeds kColsumGroupRows.
 hipError_t launch_colsum(const float* part, int64_t ld, int nseg, int n, const int* n_dev,
                          int per_tile, int width, float* tmp, float* out, hipStream_t s);
 // Row compaction (see compact_scatter_kernel): perm [N], cnt [2] = {rows that
